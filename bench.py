@@ -1,0 +1,243 @@
+"""Benchmark of the DDPM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--dtype f32|bf16]
+                    [--workload target_256] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of synthetic input
+(B=1, C=64, K=3, 256x256 by default):
+  1. ddpm_filter_fwd       materialised taps [1, 1728, 256, 256] -> [x, d1, d3, d5]
+  2. ddpm_fused_fwd        generator fused with the filter
+  3. ddpm_fused_bwd (dX)   tap recompute + gather
+  4. ddpm_fused_bwd (dY)   on-chip dK contracted with the generator weight
+  5. ddpm_fused_bwd (dW)   on-chip dK reduced into 16 float32 token partials
+  6. ddpm_reduce_partials  fixed-order sum of the partials
+Each library call runs one kernel (the reduce runs two short ones), so HIP events
+recorded around every call on the launch stream give per-kernel durations over
+the timed region.  All inputs are resident in HBM before timing starts.
+
+Printed on stdout: ONE JSON line.  ``value`` is the filter's effective bandwidth
+in TB/s (algorithmic bytes / mean filter duration); the fused forward and
+forward+backward times, per-kernel figures, the roofline of the dominant kernel
+and the fp64 oracle timed on the host cores are carried alongside.  Progress goes
+to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DDPM filter TB/s (% HBM peak) + fused fwd/bwd ms at B=1,C=64,K=3,256²"
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # dense MFMA peaks
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic(shape, dtype_bytes, S):
+    """Algorithmic bytes / flops per launch (only the method's own work)."""
+    N, C, H, W, K = shape.N, shape.C, shape.H, shape.W, shape.K
+    P = N * H * W
+    R = 3 * C * K * K
+    s = dtype_bytes
+    gemm = 2.0 * R * C * P
+    return {
+        # taps + x read, 4 planes written
+        "filter": {"bytes": (R + C + 4 * C) * s * P, "flops": 2.0 * R * P},
+        # x, y read, out written (+ weight and bias once); one generator contraction
+        "fused_fwd": {"bytes": 6 * C * s * P + (R * C + R) * s, "flops": gemm},
+        # y, G (4C) read, dX written; generator recompute
+        "bwd_dx": {"bytes": 6 * C * s * P + (R * C + R) * s, "flops": gemm},
+        # x, G_b (3C) read, dY written; W^T dK
+        "bwd_dy": {"bytes": 5 * C * s * P + R * C * s, "flops": gemm},
+        # x, y, G_b read, partials written; dK y^T
+        "bwd_dw": {"bytes": 5 * C * s * P + S * (R * C + R) * 4, "flops": gemm},
+        # partials read, gradients written
+        "reduce": {"bytes": S * (R * C + R) * 4 + (R * C + R) * s, "flops": 0.0},
+    }
+
+
+KERNEL_BOUND = {"filter": "hbm", "fused_fwd": "mfma", "bwd_dx": "mfma", "bwd_dy": "mfma", "bwd_dw": "mfma",
+                "reduce": "hbm"}
+
+
+def run_cpu_baseline(h, shape):
+    """The fp64 oracle on the same inputs: one full step, timed on the host cores."""
+    import oracle
+    orc = oracle.default()
+    a = {k: v.double().numpy() for k, v in h.items()}
+    K = shape.K
+    t = {}
+    t0 = time.perf_counter()
+    orc.filter_fwd(a["x"], a["taps"], K)
+    t["filter"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.fused_fwd(a["x"], a["y"], a["weight"], a["bias"], K)
+    t["fused_fwd"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.fused_bwd(a["x"], a["y"], a["weight"], a["bias"], a["grad_out"], K)
+    t["fused_bwd"] = time.perf_counter() - t0
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--workload", default="target_256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the DDPM hot path here is built and timed on a "
+              "single MI355X (--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import dynamic_dilated_depthwise_amd as ddpm
+    from dynamic_dilated_depthwise_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dtype = torch.float32 if args.dtype == "f32" else torch.bfloat16
+    es = 4 if args.dtype == "f32" else 2
+    shape, block = synth.WORKLOADS[args.workload]
+    N, C, H, W, K = shape.N, shape.C, shape.H, shape.W, shape.K
+    R = shape.R
+    S = ddpm.num_partials_for(N, H, W)
+    log(f"workload {args.workload} N={N} C={C} H={H} W={W} K={K} dtype={args.dtype} S={S}")
+
+    h = synth.make_inputs(shape, block, dtype, taps=True, grad=True)
+    d = {k: v.to("cuda").contiguous() for k, v in h.items()}
+    out_f = torch.empty((N, 4 * C, H, W), device="cuda", dtype=dtype)
+    out = torch.empty_like(out_f)
+    gx = torch.empty_like(d["x"])
+    gy = torch.empty_like(d["x"])
+    pw = torch.empty((S, R, C), device="cuda", dtype=torch.float32)
+    pb = torch.empty((S, R), device="cuda", dtype=torch.float32)
+    gw = torch.empty((R, C), device="cuda", dtype=dtype)
+    gb = torch.empty((R,), device="cuda", dtype=dtype)
+    stream = torch.cuda.current_stream()
+
+    calls = [
+        ("filter", lambda: ddpm.ddpm_filter_fwd(d["x"], d["taps"], out_f, K, stream)),
+        ("fused_fwd", lambda: ddpm.ddpm_fused_fwd(d["x"], d["y"], d["weight"], d["bias"], out, K, stream)),
+        ("bwd_dx", lambda: ddpm.ddpm_fused_bwd(d["x"], d["y"], d["weight"], d["bias"], d["grad_out"], gx, None,
+                                               None, None, K, stream)),
+        ("bwd_dy", lambda: ddpm.ddpm_fused_bwd(d["x"], d["y"], d["weight"], d["bias"], d["grad_out"], None, gy,
+                                               None, None, K, stream)),
+        ("bwd_dw", lambda: ddpm.ddpm_fused_bwd(d["x"], d["y"], d["weight"], d["bias"], d["grad_out"], None, None,
+                                               pw, pb, K, stream)),
+        ("reduce", lambda: ddpm.ddpm_reduce_partials(pw, pb, gw, gb, K, stream)),
+    ]
+
+    def step(events=None):
+        for i, (name, fn) in enumerate(calls):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps, events around every call on the launch stream.
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in calls]
+          for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per = {name: sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)) / args.steps
+           for i, (name, _) in enumerate(calls)}
+    log("per-call ms " + " ".join(f"{k}={v:.4f}" for k, v in per.items()))
+
+    alg = algorithmic(shape, es, S)
+    peak_t = MFMA_PEAK_TFLOPS[args.dtype]
+    kernels = {}
+    for name, ms in per.items():
+        a = alg[name]
+        gbs = a["bytes"] / (ms * 1e-3) / 1e9
+        tfl = a["flops"] / (ms * 1e-3) / 1e12
+        kb = KERNEL_BOUND[name]
+        kernels[name] = {
+            "ms": round(ms, 5), "bound": kb, "alg_bytes": int(a["bytes"]), "alg_flops": a["flops"],
+            "GB_s": round(gbs, 1), "TFLOP_s": round(tfl, 2),
+            "frac": round(gbs / HBM_PEAK_GBS if kb == "hbm" else tfl / peak_t, 4),
+        }
+
+    dom = max((n for n in per if n != "reduce"), key=lambda n: per[n])
+    kd = kernels[dom]
+    if kd["bound"] == "hbm":
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": kd["frac"], "traffic": None}
+    else:
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": kd["TFLOP_s"], "peak": peak_t, "unit": "TFLOP/s",
+                    "frac": kd["frac"], "traffic": None}
+
+    filter_tbs = kernels["filter"]["GB_s"] / 1e3
+    fwd_ms = per["fused_fwd"]
+    fwd_bwd_ms = per["fused_fwd"] + per["bwd_dx"] + per["bwd_dy"] + per["bwd_dw"] + per["reduce"]
+    gen_tflops = alg["fused_fwd"]["flops"] / (fwd_ms * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle, one full step on the host cores")
+        cores = len(os.sched_getaffinity(0))
+        omp = os.environ.get("OMP_NUM_THREADS")
+        threads = min(cores, int(omp)) if omp else cores
+        t = run_cpu_baseline(h, shape)
+        f_bytes = alg["filter"]["bytes"]
+        cpu = {"value": round(f_bytes / t["filter"] / 1e12, 5), "unit": "TB/s", "cores": threads, "kind": "oracle",
+               "sample": f"one full step of the same {args.workload} workload (filter, fused fwd, fused bwd) "
+                         "in fp64 on the host; value is the filter's algorithmic bytes / oracle filter time",
+               "filter_s": round(t["filter"], 3), "fused_fwd_s": round(t["fused_fwd"], 3),
+               "fused_bwd_s": round(t["fused_bwd"], 3)}
+        log(f"cpu baseline {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(filter_tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic (seeded Gaussian tensors of the workload's shapes)",
+        "config": {"workload": f"DDPM {args.workload}: B={N} C={C} K={K} {H}x{W}, "
+                               "filter + fused fwd + fused bwd (dX, dY, dW partials) + reduce",
+                   "N": N, "C": C, "H": H, "W": W, "K": K, "num_partials": S},
+        "filter_ms": round(per["filter"], 5),
+        "filter_hbm_frac": kernels["filter"]["frac"],
+        "fused_fwd_ms": round(fwd_ms, 5),
+        "fused_fwd_bwd_ms": round(fwd_bwd_ms, 5),
+        "fused_fwd_mfma_tflops": round(gen_tflops, 2),
+        "fused_fwd_mfma_frac": round(gen_tflops / peak_t, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

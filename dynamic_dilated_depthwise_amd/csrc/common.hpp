@@ -1,0 +1,144 @@
+// common.hpp -- device helpers shared by the DDPM kernels (gfx950 / CDNA4, wave64).
+//
+// Storage types: float for float32 tensors, uint16_t for bfloat16 tensors (raw
+// bits).  Arithmetic is always float32; bf16 values widen exactly and narrow with
+// the hardware round-to-nearest-even conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ddpm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+typedef uint16_t bf16_t;
+
+constexpr int kWave = 64;
+
+// Branch b uses dilation 1 + 2b, i.e. (1, 3, 5).
+__host__ __device__ constexpr int dilation(int b) { return 1 + 2 * b; }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
+    return __uint_as_float((uint32_t)u << 16);
+}
+// Round-to-nearest-even narrowing (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ float round_to_bf16(float f) {
+    return bf16_bits_to_f32(f32_to_bf16_bits(f));
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr bool is_bf16 = false;
+    __device__ __forceinline__ static float to_f32(float v) { return v; }
+    __device__ __forceinline__ static float from_f32(float v) { return v; }
+    // Value as it is used inside the method after the dtype's own rounding.
+    __device__ __forceinline__ static float quant(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+    static constexpr bool is_bf16 = true;
+    __device__ __forceinline__ static float to_f32(bf16_t v) { return bf16_bits_to_f32(v); }
+    __device__ __forceinline__ static bf16_t from_f32(float v) { return f32_to_bf16_bits(v); }
+    __device__ __forceinline__ static float quant(float v) { return round_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// lane l receives D[4*(l/16) + v][l%16] in component v.
+__device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8*(l/16) + e] and
+// B[8*(l/16) + e][l%16] for e = 0..7; D as for the f32 variant.
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const uint16_t (&v)[8]) {
+    u16x8 u;
+    u[0] = v[0]; u[1] = v[1]; u[2] = v[2]; u[3] = v[3];
+    u[4] = v[4]; u[5] = v[5]; u[6] = v[6]; u[7] = v[7];
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// ---------------------------------------------------------------------------- loads
+// Four consecutive pixels w..w+3 of one image row `row` (a pointer to element 0 of
+// the row), widened to float; pixels outside [0, W) and rows that are not valid
+// read as zero.  `aligned4` promises that w is a multiple of 4 and the row start
+// is 16-byte aligned for float (8-byte for bf16) so a single vector load is legal.
+template <typename T>
+__device__ __forceinline__ f32x4 load4_row(const T *__restrict__ row, int w, int W, bool row_ok,
+                                           bool aligned4) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (!row_ok) return v;
+    if (w >= 0 && w + 3 < W) {
+        if constexpr (Elem<T>::is_bf16) {
+            if (aligned4) {
+                u16x4 u = *(const u16x4 *)(row + w);
+                v[0] = bf16_bits_to_f32(u[0]); v[1] = bf16_bits_to_f32(u[1]);
+                v[2] = bf16_bits_to_f32(u[2]); v[3] = bf16_bits_to_f32(u[3]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = bf16_bits_to_f32(row[w + k]);
+            }
+        } else {
+            if (aligned4) {
+                v = *(const f32x4 *)(row + w);
+            } else {
+                f32x4_a4 t = *(const f32x4_a4 *)(row + w);
+                v = t;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int ww = w + k;
+            if (ww >= 0 && ww < W) v[k] = Elem<T>::to_f32(row[ww]);
+        }
+    }
+    return v;
+}
+
+// Raw (bit-exact) copy helpers for the x block of the output.
+template <typename T>
+__device__ __forceinline__ void copy4_row(const T *__restrict__ src, T *__restrict__ dst, int w, int W,
+                                          bool aligned4) {
+    if (w + 3 < W && aligned4) {
+        if constexpr (Elem<T>::is_bf16) {
+            *(u16x4 *)(dst + w) = *(const u16x4 *)(src + w);
+        } else {
+            *(f32x4 *)(dst + w) = *(const f32x4 *)(src + w);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (w + k < W) dst[w + k] = src[w + k];
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4_row(T *__restrict__ row, int w, int W, f32x4 v, bool aligned4) {
+    if (w + 3 < W && aligned4) {
+        if constexpr (Elem<T>::is_bf16) {
+            u16x4 u;
+            u[0] = f32_to_bf16_bits(v[0]); u[1] = f32_to_bf16_bits(v[1]);
+            u[2] = f32_to_bf16_bits(v[2]); u[3] = f32_to_bf16_bits(v[3]);
+            *(u16x4 *)(row + w) = u;
+        } else {
+            *(f32x4 *)(row + w) = v;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (w + k < W) row[w + k] = Elem<T>::from_f32(v[k]);
+    }
+}
+
+}  // namespace ddpm

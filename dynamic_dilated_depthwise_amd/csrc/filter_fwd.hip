@@ -1,0 +1,192 @@
+// filter_fwd.hip -- dynamic dilated filter with materialised taps (gfx950).
+//
+// Operation (page "lartpang/DynamicConvolutionOperator", section "CUDA 动态过滤"):
+// with the taps already generated, one pass serves the three dilations (1, 3, 5)
+// from one spatial tile, accumulates in float32 and writes [x, d1, d3, d5].
+//
+// The pass is a pure stream: per pixel and channel it reads 3*K*K taps and one x
+// value and writes four outputs, so it is bound by HBM bandwidth.  Design:
+//   * one workgroup = one (n, c) plane x a TH x TW pixel tile;
+//   * the x tile plus a 5*(K-1)/2 halo is staged once in LDS (as float), so every
+//     dilation's neighbourhood is read from LDS, never re-fetched from HBM;
+//   * each thread owns VEC consecutive pixels of a row and streams the taps with
+//     16-byte non-temporal loads (they are touched exactly once), and writes the
+//     four output planes with non-temporal vector stores;
+//   * the x block of the output is copied from the staged tile bit-exactly.
+#include "common.hpp"
+#include "launchers.hpp"
+
+namespace ddpm {
+
+template <typename T, int VEC> struct VecOf;
+template <> struct VecOf<float, 4> { typedef float type __attribute__((ext_vector_type(4))); };
+template <> struct VecOf<float, 2> { typedef float type __attribute__((ext_vector_type(2))); };
+template <> struct VecOf<float, 1> { typedef float type; };
+template <> struct VecOf<bf16_t, 8> { typedef uint16_t type __attribute__((ext_vector_type(8))); };
+template <> struct VecOf<bf16_t, 4> { typedef uint16_t type __attribute__((ext_vector_type(4))); };
+template <> struct VecOf<bf16_t, 2> { typedef uint16_t type __attribute__((ext_vector_type(2))); };
+template <> struct VecOf<bf16_t, 1> { typedef uint16_t type; };
+
+template <typename V, typename T, int VEC>
+__device__ __forceinline__ T lane_of(const V &v, int k) {
+    if constexpr (VEC == 1) return v; else return v[k];
+}
+template <typename V, typename T, int VEC>
+__device__ __forceinline__ void set_lane(V &v, int k, T val) {
+    if constexpr (VEC == 1) v = val; else v[k] = val;
+}
+
+// Exact narrowing of a value that was widened from T (used for the x copy).
+template <typename T> __device__ __forceinline__ T exact_narrow(float v);
+template <> __device__ __forceinline__ float exact_narrow<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t exact_narrow<bf16_t>(float v) {
+    return (bf16_t)(__float_as_uint(v) >> 16);
+}
+
+template <typename T, int K, int VEC>
+__global__ __launch_bounds__(256) void filter_fwd_kernel(const T *__restrict__ x, const T *__restrict__ taps,
+                                                         T *__restrict__ out, int C, int H, int W, int TH,
+                                                         int TW) {
+    constexpr int r = (K - 1) / 2;
+    constexpr int HALO = 5 * r;
+    constexpr int KK = K * K;
+    typedef typename VecOf<T, VEC>::type V;
+    extern __shared__ float xs[];
+
+    const int LW = TW + 2 * HALO;
+    const int LH = TH + 2 * HALO;
+    const int nc = blockIdx.z;
+    const int n = nc / C;
+    const int c = nc - n * C;
+    const int h0 = blockIdx.y * TH;
+    const int w0 = blockIdx.x * TW;
+    const int64_t HW = (int64_t)H * W;
+
+    const T *__restrict__ xp = x + (int64_t)nc * HW;
+    for (int i = threadIdx.x; i < LH * LW; i += blockDim.x) {
+        const int lr = i / LW;
+        const int lc = i - lr * LW;
+        const int hh = h0 - HALO + lr;
+        const int ww = w0 - HALO + lc;
+        float v = 0.f;
+        if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = Elem<T>::to_f32(xp[(int64_t)hh * W + ww]);
+        xs[i] = v;
+    }
+    __syncthreads();
+
+    const int64_t R = 3LL * C * KK;
+    const T *__restrict__ tp = taps + (int64_t)n * R * HW;
+    T *__restrict__ op = out + (int64_t)n * 4 * C * HW;
+    const int gpr = TW / VEC;
+    for (int gi = threadIdx.x; gi < TH * gpr; gi += blockDim.x) {
+        const int lr = gi / gpr;
+        const int lc = (gi - lr * gpr) * VEC;
+        const int h = h0 + lr;
+        const int w = w0 + lc;
+        if (h >= H || w >= W) continue;  // W % VEC == 0: a vector is wholly in or out
+        const int64_t pix = (int64_t)h * W + w;
+        const float *xc = xs + (lr + HALO) * LW + (lc + HALO);
+
+        float acc[3][VEC];
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+            const int D = dilation(b);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[b][k] = 0.f;
+#pragma unroll
+            for (int t = 0; t < KK; ++t) {
+                const int ki = t / K, kj = t % K;
+                const int64_t plane = (int64_t)(b * C + c) * KK + t;
+                const V tv = __builtin_nontemporal_load((const V *)(tp + plane * HW + pix));
+                const float *xn = xc + (ki - r) * D * LW + (kj - r) * D;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k)
+                    acc[b][k] += Elem<T>::to_f32(lane_of<V, T, VEC>(tv, k)) * xn[k];
+            }
+        }
+        V xv;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) set_lane<V, T, VEC>(xv, k, exact_narrow<T>(xc[k]));
+        __builtin_nontemporal_store(xv, (V *)(op + (int64_t)c * HW + pix));
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+            V ov;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) set_lane<V, T, VEC>(ov, k, Elem<T>::from_f32(acc[b][k]));
+            __builtin_nontemporal_store(ov, (V *)(op + (int64_t)((1 + b) * C + c) * HW + pix));
+        }
+    }
+}
+
+// Tile choice: TW is the row segment one workgroup covers (power of two, at most
+// 64 vectors), TH the number of rows; TH shrinks until the launch has enough
+// workgroups to give every CU several, since the halo rows are the only cost of
+// a short tile.
+static void filter_tile(int64_t planes, int H, int W, int VEC, int &TH, int &TW) {
+    int tw = VEC;
+    while (tw < W && tw < 64 * VEC) tw *= 2;
+    TW = tw;
+    const int rows_per_pass = 256 / (TW / VEC) > 0 ? 256 / (TW / VEC) : 1;
+    int th = 4 * rows_per_pass;
+    while (th > rows_per_pass && th / 2 >= 1) {
+        const int64_t wgs = planes * ((H + th - 1) / th) * ((W + TW - 1) / TW);
+        if (wgs >= 2048) break;
+        th /= 2;
+    }
+    TH = th < 1 ? 1 : th;
+}
+
+template <typename T, int K, int VEC>
+static hipError_t launch_filter_t(const void *x, const void *taps, void *out, int N, int C, int H, int W,
+                                  hipStream_t stream) {
+    int TH, TW;
+    filter_tile((int64_t)N * C, H, W, VEC, TH, TW);
+    constexpr int HALO = 5 * ((K - 1) / 2);
+    const size_t lds = sizeof(float) * (size_t)(TH + 2 * HALO) * (TW + 2 * HALO);
+    auto kern = filter_fwd_kernel<T, K, VEC>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((W + TW - 1) / TW, (H + TH - 1) / TH, N * C);
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, (const T *)x, (const T *)taps, (T *)out, C, H, W, TH,
+                       TW);
+    return hipGetLastError();
+}
+
+template <typename T, int K>
+static hipError_t launch_filter_k(const void *x, const void *taps, void *out, int N, int C, int H, int W,
+                                  hipStream_t stream, int vec) {
+    if constexpr (Elem<T>::is_bf16) {
+        switch (vec) {
+            case 8: return launch_filter_t<T, K, 8>(x, taps, out, N, C, H, W, stream);
+            case 4: return launch_filter_t<T, K, 4>(x, taps, out, N, C, H, W, stream);
+            case 2: return launch_filter_t<T, K, 2>(x, taps, out, N, C, H, W, stream);
+            default: return launch_filter_t<T, K, 1>(x, taps, out, N, C, H, W, stream);
+        }
+    } else {
+        switch (vec) {
+            case 4: return launch_filter_t<T, K, 4>(x, taps, out, N, C, H, W, stream);
+            case 2: return launch_filter_t<T, K, 2>(x, taps, out, N, C, H, W, stream);
+            default: return launch_filter_t<T, K, 1>(x, taps, out, N, C, H, W, stream);
+        }
+    }
+}
+
+hipError_t launch_filter_fwd(const void *x, const void *taps, void *out, int N, int C, int H, int W, int K,
+                             bool bf16, int vec, hipStream_t stream) {
+    if (bf16) {
+        switch (K) {
+            case 1: return launch_filter_k<bf16_t, 1>(x, taps, out, N, C, H, W, stream, vec);
+            case 3: return launch_filter_k<bf16_t, 3>(x, taps, out, N, C, H, W, stream, vec);
+            default: return launch_filter_k<bf16_t, 5>(x, taps, out, N, C, H, W, stream, vec);
+        }
+    }
+    switch (K) {
+        case 1: return launch_filter_k<float, 1>(x, taps, out, N, C, H, W, stream, vec);
+        case 3: return launch_filter_k<float, 3>(x, taps, out, N, C, H, W, stream, vec);
+        default: return launch_filter_k<float, 5>(x, taps, out, N, C, H, W, stream, vec);
+    }
+}
+
+}  // namespace ddpm

@@ -1,0 +1,510 @@
+// fused_bwd.hip -- training backward of the fused DDPM with tap recompute (gfx950).
+//
+// Operation (page "lartpang/DynamicConvolutionOperator", section
+// "CUDA Flash 式融合训练"): no tap tensor is saved; the backward
+//   * dX: recomputes the dynamic taps and gathers each dilation's contribution,
+//       dX[c,q] = G_x[c,q] + sum_{b,t} T[o, q-d_bt] * G_b[c, q-d_bt];
+//   * dY: forms dK = shifted(x) * grad on chip and contracts it with the
+//       generator weight at once, dY[c',p] = sum_o W[o,c'] * dK[o,p];
+//   * dWeight / dbias: forms dK on chip and reduces it over space into at most 16
+//       float32 partials over contiguous token ranges (the second short kernel,
+//       reduce.hip, sums them).
+// Every output element is stored once; nothing is accumulated through atomics, so
+// results are bit-identical from run to run.
+#include "gen_mma.hpp"
+#include "launchers.hpp"
+
+namespace ddpm {
+
+constexpr int kRows = 4;   // one row per wave
+constexpr int kCols = 64;  // 16 lanes x 4 pixels
+
+// ============================================================================ dX
+// Same tile as the fused forward.  For every (b, t) the generator block is run
+// with y read at the pixel shifted by -d_bt, so each lane holds the tap that
+// was applied at the source pixel q - d_bt; it is multiplied by G_b at that
+// same source pixel.  Zero-padded G kills every term whose source pixel lies
+// outside the image (the recomputed tap there would be the bias alone).
+template <typename T, int K, int KQ>
+__global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y, const T *__restrict__ wg,
+                                                        const T *__restrict__ bg, const T *__restrict__ gout,
+                                                        T *__restrict__ gx, int C, int H, int W, int al) {
+    using G = Gen<T>;
+    constexpr int r = (K - 1) / 2;
+    constexpr int KK = K * K;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int nCB = (C + 15) >> 4;
+    const int n = blockIdx.z / nCB;
+    const int c0 = (blockIdx.z - n * nCB) * 16;
+    const int h = blockIdx.y * kRows + wave;
+    const int w = blockIdx.x * kCols + 4 * j;
+    if (h >= H) return;  // no barriers in this kernel
+    const int64_t HW = (int64_t)H * W;
+    const bool aligned4 = al != 0;
+    const bool cvec = Elem<T>::is_bf16 ? (al != 0 && (C & 7) == 0) : (al != 0 && (C & 3) == 0);
+    const T *__restrict__ yn = y + (int64_t)n * C * HW;
+    const T *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
+    const int nq = KQ > 0 ? KQ : (C + G::CH - 1) / G::CH;
+    const int cA = c0 + j;
+
+    float dacc[4][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) dacc[v][pb] = 0.f;
+
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+        const int D = dilation(b);
+#pragma unroll 1
+        for (int t = 0; t < KK; ++t) {
+            const int ki = t / K;
+            const int kj = t - ki * K;
+            const int dr = (ki - r) * D;
+            const int dc = (kj - r) * D;
+            const int hs = h - dr;
+            const int ws = w - dc;
+            const bool rs_ok = hs >= 0 && hs < H;
+            const bool al_s = aligned4 && ((dc & 3) == 0);
+            const int64_t rowoff = (int64_t)(rs_ok ? hs : 0) * W;
+
+            const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
+            float bias[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int c = c0 + 4 * g + v;
+                bias[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+            }
+            f32x4 acc[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
+#pragma unroll
+            for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) {
+                if (KQ > 0 || q < nq) {
+                    G::mma(acc, G::load_A(arow, q, g, C, cvec), G::load_B(yn, q, g, C, HW, rowoff, ws, W, rs_ok, al_s));
+                }
+            }
+            if constexpr (KQ == 0) {
+                for (int q = 1; q < nq; ++q)
+                    G::mma(acc, G::load_A(arow, q, g, C, cvec), G::load_B(yn, q, g, C, HW, rowoff, ws, W, rs_ok, al_s));
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int c = c0 + 4 * g + v;
+                const f32x4 gs = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, ws, W,
+                                           rs_ok && c < C, al_s);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += Elem<T>::quant(acc[pb][v]) * gs[pb];
+            }
+        }
+    }
+
+    const int64_t rowoff = (int64_t)h * W;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int c = c0 + 4 * g + v;
+        if (c >= C) continue;
+        const f32x4 gxs = load4_row(gn + (int64_t)c * HW + rowoff, w, W, true, aligned4);
+        f32x4 o;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) o[pb] = dacc[v][pb] + gxs[pb];
+        store4_row(gx + ((int64_t)n * C + c) * HW + rowoff, w, W, o, aligned4);
+    }
+}
+
+// ============================================================================ dY
+// dY = W^T dK as an MFMA product: rows = output channels c' (16 per block, MB
+// blocks per wave), columns = the wave's 64 pixels (4 per lane), contraction over
+// the generator rows o = (b, c, t).  The B operand dK[o, p] = G_b[c, p] *
+// x[c, p + d_bt] is formed in registers from G and the shifted x and never stored.
+//   float32: one k-step = 4 generator rows (b, 4cq + g, t), lane group g;
+//   bfloat16: one k-step = 32 generator rows (b, 32cq + 8g + e, t); dK is rounded
+//   to bfloat16 as the MFMA operand.
+template <typename T, int K, int MB>
+__global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x, const T *__restrict__ wg,
+                                                        const T *__restrict__ gout, T *__restrict__ gy, int C, int H,
+                                                        int W, int al) {
+    constexpr int r = (K - 1) / 2;
+    constexpr int KK = K * K;
+    constexpr bool BF = Elem<T>::is_bf16;
+    constexpr int CK = BF ? 32 : 4;  // generator channels per k-step
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int nMG = (C + 63) >> 6;
+    const int n = blockIdx.z / nMG;
+    const int cm0 = (blockIdx.z - n * nMG) * 64;
+    const int h = blockIdx.y * kRows + wave;
+    const int w = blockIdx.x * kCols + 4 * j;
+    if (h >= H) return;
+    const int64_t HW = (int64_t)H * W;
+    const bool aligned4 = al != 0;
+    const T *__restrict__ xn = x + (int64_t)n * C * HW;
+    const T *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
+    const int64_t rowoff = (int64_t)h * W;
+
+    f32x4 acc[MB][4];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) acc[m][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ncq = (C + CK - 1) / CK;
+#pragma unroll 1
+    for (int cq = 0; cq < ncq; ++cq) {
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+            const int D = dilation(b);
+            if constexpr (!BF) {
+                const int c = CK * cq + g;
+                const bool c_ok = c < C;
+                const f32x4 gb = load4_row(gn + (int64_t)((1 + b) * C + (c_ok ? c : 0)) * HW + rowoff, w, W, c_ok,
+                                           aligned4);
+#pragma unroll 1
+                for (int t = 0; t < KK; ++t) {
+                    const int ki = t / K;
+                    const int kj = t - ki * K;
+                    const int hh = h + (ki - r) * D;
+                    const int dc = (kj - r) * D;
+                    const bool rok = c_ok && hh >= 0 && hh < H;
+                    const f32x4 xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(rok ? hh : 0) * W,
+                                               w + dc, W, rok, aligned4 && ((dc & 3) == 0));
+                    const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) {
+                        const int cp = cm0 + 16 * m + j;
+                        const float a = (c_ok && cp < C) ? wrow[cp] : 0.f;
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x4_f32(a, gb[pb] * xs[pb], acc[m][pb]);
+                    }
+                }
+            } else {
+                f32x4 gb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = CK * cq + 8 * g + e;
+                    gb[e] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, w, W, c < C,
+                                      aligned4);
+                }
+#pragma unroll 1
+                for (int t = 0; t < KK; ++t) {
+                    const int ki = t / K;
+                    const int kj = t - ki * K;
+                    const int hh = h + (ki - r) * D;
+                    const int dc = (kj - r) * D;
+                    const bool hok = hh >= 0 && hh < H;
+                    uint16_t bv[4][8];
+                    uint16_t av[MB][8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int c = CK * cq + 8 * g + e;
+                        const bool c_ok = c < C;
+                        const f32x4 xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(hok ? hh : 0) * W,
+                                                   w + dc, W, c_ok && hok, aligned4 && ((dc & 3) == 0));
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
+                        const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) {
+                            const int cp = cm0 + 16 * m + j;
+                            av[m][e] = (c_ok && cp < C) ? wrow[cp] : (uint16_t)0;
+                        }
+                    }
+                    bf16x8 bq[4];
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) bq[pb] = pack_bf16x8(bv[pb]);
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) {
+                        const bf16x8 aq = pack_bf16x8(av[m]);
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x32_bf16(aq, bq[pb], acc[m][pb]);
+                    }
+                }
+            }
+        }
+    }
+
+    T *__restrict__ yo = gy + (int64_t)n * C * HW;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int cp = cm0 + 16 * m + 4 * g + v;
+            if (cp >= C) continue;
+            store4_row(yo + (int64_t)cp * HW + rowoff, w, W,
+                       f32x4{acc[m][0][v], acc[m][1][v], acc[m][2][v], acc[m][3][v]}, aligned4);
+        }
+    }
+}
+
+// ============================================================================ dW / db
+// One workgroup = CG generator (branch, tap) pairs x 16 depthwise channels x up to
+// 64 input channels c' of the weight gradient x one token split s.  The four waves
+// take interleaved chunks of the split's tokens and are summed in a fixed order
+// through LDS at the end, so each partial element is stored exactly once.
+//   MFMA rows    = channel c0 + i of one (b, t) pair (i = lane%16 as A supplier);
+//   MFMA columns = c' = cn0 + 16*nb + j (j = lane%16 as B supplier);
+//   contraction  = tokens: float32 4 per k-step (lane group g), four k-steps per
+//                  16-token chunk; bfloat16 32 per k-step (8 per lane group).
+template <typename T, int K, int CG, int NB>
+__global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, const T *__restrict__ y,
+                                                     const T *__restrict__ gout, float *__restrict__ dw_part,
+                                                     float *__restrict__ db_part, int N, int C, int H, int W, int S) {
+    constexpr int r = (K - 1) / 2;
+    constexpr int KK = K * K;
+    constexpr int NCOMBO = 3 * KK;
+    constexpr bool BF = Elem<T>::is_bf16;
+    constexpr int RL = BF ? 8 : 4;  // tokens per lane per chunk
+    constexpr int KC = 4 * RL;      // tokens per wave per chunk
+    __shared__ float red[4][NB * 4][64];
+    __shared__ float redb[4][4][16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int combo0 = blockIdx.x * CG;
+    const int nCB = (C + 15) >> 4;
+    const int cb = blockIdx.y % nCB;
+    const int c0 = cb * 16;
+    const int cn0 = (blockIdx.y / nCB) * 64;
+    const int s = blockIdx.z;
+    const int64_t HW = (int64_t)H * W;
+    const int64_t CHW = (int64_t)C * HW;
+    const int64_t ntok = (int64_t)N * HW;
+    const int64_t t0 = ntok * s / S;
+    const int64_t t1 = ntok * (s + 1) / S;
+    const int64_t R = 3LL * C * KK;
+
+    // Per combo: branch, row/column shift; invalid combos get b = -1.
+    int cb_b[CG], cb_dr[CG], cb_dc[CG];
+#pragma unroll
+    for (int cc = 0; cc < CG; ++cc) {
+        const int combo = combo0 + cc;
+        if (combo < NCOMBO) {
+            const int b = combo / KK;
+            const int t = combo - b * KK;
+            const int ki = t / K;
+            const int kj = t - ki * K;
+            cb_b[cc] = b;
+            cb_dr[cc] = (ki - r) * dilation(b);
+            cb_dc[cc] = (kj - r) * dilation(b);
+        } else {
+            cb_b[cc] = -1;
+            cb_dr[cc] = 0;
+            cb_dc[cc] = 0;
+        }
+    }
+    const int cA = c0 + j;         // A role: depthwise channel
+    const bool cA_ok = cA < C;
+
+    f32x4 acc[CG][NB];
+    float dbacc[CG];
+#pragma unroll
+    for (int cc = 0; cc < CG; ++cc) {
+        dbacc[cc] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[cc][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int64_t p0 = t0 + (int64_t)wave * KC; p0 < t1; p0 += 4 * KC) {
+        const int64_t pf = p0 + (int64_t)g * RL;  // this lane's first token
+        float a[CG][RL];
+        float bvals[NB][RL];
+#pragma unroll
+        for (int cc = 0; cc < CG; ++cc)
+#pragma unroll
+            for (int k = 0; k < RL; ++k) a[cc][k] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int k = 0; k < RL; ++k) bvals[nb][k] = 0.f;
+
+        if (pf < t1) {
+            int n = (int)(pf / HW);
+            int64_t rem = pf - (int64_t)n * HW;
+            int hh = (int)(rem / W);
+            int ww = (int)(rem - (int64_t)hh * W);
+#pragma unroll
+            for (int k = 0; k < RL; ++k) {
+                if (pf + k < t1) {
+                    const T *xn = x + (int64_t)n * CHW;
+                    const T *gn = gout + (int64_t)n * 4 * CHW;
+                    const int64_t pix = (int64_t)hh * W + ww;
+#pragma unroll
+                    for (int cc = 0; cc < CG; ++cc) {
+                        const int b = cb_b[cc];
+                        if (b >= 0 && cA_ok) {
+                            const int hs = hh + cb_dr[cc];
+                            const int ws = ww + cb_dc[cc];
+                            if (hs >= 0 && hs < H && ws >= 0 && ws < W) {
+                                const float gv = Elem<T>::to_f32(gn[(int64_t)((1 + b) * C + cA) * HW + pix]);
+                                const float xv = Elem<T>::to_f32(xn[(int64_t)cA * HW + (int64_t)hs * W + ws]);
+                                a[cc][k] = gv * xv;
+                            }
+                        }
+                    }
+                    const T *yn = y + (int64_t)n * CHW;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int cp = cn0 + 16 * nb + j;
+                        if (cp < C) bvals[nb][k] = Elem<T>::to_f32(yn[(int64_t)cp * HW + pix]);
+                    }
+                }
+                if (++ww == W) {
+                    ww = 0;
+                    if (++hh == H) {
+                        hh = 0;
+                        ++n;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < CG; ++cc)
+#pragma unroll
+            for (int k = 0; k < RL; ++k) dbacc[cc] += a[cc][k];
+        if constexpr (!BF) {
+#pragma unroll
+            for (int k = 0; k < RL; ++k)
+#pragma unroll
+                for (int cc = 0; cc < CG; ++cc)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[cc][nb] = mfma_16x16x4_f32(a[cc][k], bvals[nb][k], acc[cc][nb]);
+        } else {
+            bf16x8 bq[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                uint16_t u[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) u[k] = f32_to_bf16_bits(bvals[nb][k]);  // exact: y is bf16
+                bq[nb] = pack_bf16x8(u);
+            }
+#pragma unroll
+            for (int cc = 0; cc < CG; ++cc) {
+                uint16_t u[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) u[k] = f32_to_bf16_bits(a[cc][k]);
+                const bf16x8 aq = pack_bf16x8(u);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[cc][nb] = mfma_16x16x32_bf16(aq, bq[nb], acc[cc][nb]);
+            }
+        }
+    }
+
+    // Fixed-order reduction over the four waves, one (b, t) pair at a time.
+    float *dwp = dw_part + (int64_t)s * R * C;
+    float *dbp = db_part + (int64_t)s * R;
+#pragma unroll
+    for (int cc = 0; cc < CG; ++cc) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[wave][nb * 4 + v][lane] = acc[cc][nb][v];
+        redb[wave][g][j] = dbacc[cc];
+        __syncthreads();
+        const int combo = combo0 + cc;
+        if (combo < NCOMBO) {
+            const int b = combo / KK;
+            const int t = combo - b * KK;
+            if (wave < NB) {
+                const int nb = wave;
+                const int cp = cn0 + 16 * nb + j;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int c = c0 + 4 * g + v;
+                    const float sum = ((red[0][nb * 4 + v][lane] + red[1][nb * 4 + v][lane]) + red[2][nb * 4 + v][lane]) +
+                                      red[3][nb * 4 + v][lane];
+                    if (c < C && cp < C) dwp[((int64_t)(b * C + c) * KK + t) * C + cp] = sum;
+                }
+            }
+            if (wave == 0 && g == 0 && cn0 == 0 && cA_ok) {
+                float sb = 0.f;
+#pragma unroll
+                for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+                    for (int gg = 0; gg < 4; ++gg) sb += redb[wv][gg][j];
+                dbp[(int64_t)(b * C + cA) * KK + t] = sb;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ============================================================================ launch
+template <typename T, int K>
+static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, const void *bg, const void *gout,
+                               void *gx, void *gy, float *dwp, float *dbp, int S, int N, int C, int H, int W, bool al,
+                               hipStream_t stream) {
+    const int iA = al ? 1 : 0;
+    // dX
+    if (gx != nullptr) {
+        dim3 grid((W + kCols - 1) / kCols, (H + kRows - 1) / kRows, N * ((C + 15) / 16));
+        const int nq = (C + Gen<T>::CH - 1) / Gen<T>::CH;
+        auto args = [&](auto kern) {
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)y, (const T *)wg, (const T *)bg,
+                               (const T *)gout, (T *)gx, C, H, W, iA);
+        };
+        if (nq == 1) args(bwd_dx_kernel<T, K, 1>);
+        else if (nq == 2) args(bwd_dx_kernel<T, K, 2>);
+        else if (!Elem<T>::is_bf16 && nq <= 4) args(bwd_dx_kernel<T, K, 4>);
+        else args(bwd_dx_kernel<T, K, 0>);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // dY
+    if (gy != nullptr) {
+        dim3 grid((W + kCols - 1) / kCols, (H + kRows - 1) / kRows, N * ((C + 63) / 64));
+        const int mb = (C >= 64) ? 4 : (C + 15) / 16;
+        auto args = [&](auto kern) {
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)x, (const T *)wg, (const T *)gout,
+                               (T *)gy, C, H, W, iA);
+        };
+        if (mb == 1) args(bwd_dy_kernel<T, K, 1>);
+        else if (mb == 2) args(bwd_dy_kernel<T, K, 2>);
+        else args(bwd_dy_kernel<T, K, 4>);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // dW / db partials
+    if (dwp != nullptr) {
+        constexpr int CG = 4;
+        constexpr int NCOMBO = 3 * K * K;
+        dim3 grid((NCOMBO + CG - 1) / CG, ((C + 15) / 16) * ((C + 63) / 64), S);
+        const int nb = (C >= 64) ? 4 : (C + 15) / 16;
+        auto args = [&](auto kern) {
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)x, (const T *)y, (const T *)gout, dwp, dbp,
+                               N, C, H, W, S);
+        };
+        if (nb == 1) args(bwd_dw_kernel<T, K, CG, 1>);
+        else if (nb == 2) args(bwd_dw_kernel<T, K, CG, 2>);
+        else args(bwd_dw_kernel<T, K, CG, 4>);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_fused_bwd(const void *x, const void *y, const void *wg, const void *bg, const void *gout, void *gx,
+                            void *gy, float *dw_part, float *db_part, int S, int N, int C, int H, int W, int K,
+                            bool bf16, bool al, hipStream_t stream) {
+    if (bf16) {
+        switch (K) {
+            case 1: return launch_bwd_k<bf16_t, 1>(x, y, wg, bg, gout, gx, gy, dw_part, db_part, S, N, C, H, W, al, stream);
+            case 3: return launch_bwd_k<bf16_t, 3>(x, y, wg, bg, gout, gx, gy, dw_part, db_part, S, N, C, H, W, al, stream);
+            default: return launch_bwd_k<bf16_t, 5>(x, y, wg, bg, gout, gx, gy, dw_part, db_part, S, N, C, H, W, al, stream);
+        }
+    }
+    switch (K) {
+        case 1: return launch_bwd_k<float, 1>(x, y, wg, bg, gout, gx, gy, dw_part, db_part, S, N, C, H, W, al, stream);
+        case 3: return launch_bwd_k<float, 3>(x, y, wg, bg, gout, gx, gy, dw_part, db_part, S, N, C, H, W, al, stream);
+        default: return launch_bwd_k<float, 5>(x, y, wg, bg, gout, gx, gy, dw_part, db_part, S, N, C, H, W, al, stream);
+    }
+}
+
+}  // namespace ddpm

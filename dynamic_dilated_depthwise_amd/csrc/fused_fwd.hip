@@ -1,0 +1,197 @@
+// fused_fwd.hip -- 1x1 generator fused with the dynamic dilated filter (gfx950).
+//
+// Operation (page "lartpang/DynamicConvolutionOperator", section
+// "CUDA 融合生成器推理"): per channel tile x spatial tile, weight x y-tile gives the
+// dynamic taps, which are consumed at once with the shifted x; the taps live only
+// in registers and never reach global memory.  Output [x, d1, d3, d5].
+//
+// Work decomposition
+//   workgroup = 4 waves = image n, 16 depthwise channels c0.., 4 rows x 64 columns;
+//   wave      = one row of the tile (64 pixels, four per lane);
+//   per (branch b, tap t) the wave runs the generator block for its 16 channels
+//   (see gen_mma.hpp), adds the bias, rounds the taps to the dtype, and
+//   multiplies them with x at the dilated offset, read from an LDS copy of the
+//   x tile with its 5*(K-1)/2 halo.  The three branch sums stay in registers.
+// y is read once per wave into registers (the MFMA B operand is the same for
+// all 3*K*K generator blocks) when C <= 64; larger C streams it per block.
+#include "gen_mma.hpp"
+#include "launchers.hpp"
+
+namespace ddpm {
+
+constexpr int kTileRows = 4;   // one row per wave
+constexpr int kTileCols = 64;  // 16 lanes x 4 pixels
+
+template <int K> struct XTile {
+    static constexpr int r = (K - 1) / 2;
+    static constexpr int HALO = 5 * r;
+    static constexpr int LH = kTileRows + 2 * HALO;
+    static constexpr int LW = kTileCols + 2 * HALO;
+    static constexpr int PLANE = LH * LW;
+    static constexpr size_t bytes = sizeof(float) * 16 * PLANE;
+};
+
+// Stage x[n, c0..c0+15, h0-HALO .., w0-HALO ..] into LDS as float, zero outside.
+template <typename T, int K>
+__device__ __forceinline__ void stage_x_tile(float *xs, const T *__restrict__ xn, int c0, int C, int H, int W,
+                                             int64_t HW, int h0, int w0) {
+    using X = XTile<K>;
+    for (int i = threadIdx.x; i < 16 * X::PLANE; i += blockDim.x) {
+        const int ch = i / X::PLANE;
+        const int rem = i - ch * X::PLANE;
+        const int lr = rem / X::LW;
+        const int lc = rem - lr * X::LW;
+        const int c = c0 + ch;
+        const int hh = h0 - X::HALO + lr;
+        const int ww = w0 - X::HALO + lc;
+        float v = 0.f;
+        if (c < C && hh >= 0 && hh < H && ww >= 0 && ww < W) v = Elem<T>::to_f32(xn[(int64_t)c * HW + (int64_t)hh * W + ww]);
+        xs[i] = v;
+    }
+}
+
+template <typename T, int K, int KQ>
+__global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__ x, const T *__restrict__ y,
+                                                           const T *__restrict__ wg, const T *__restrict__ bg,
+                                                           T *__restrict__ out, int C, int H, int W, int al) {
+    using G = Gen<T>;
+    using X = XTile<K>;
+    constexpr int r = X::r;
+    constexpr int KK = K * K;
+    extern __shared__ float xs[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int nCB = (C + 15) >> 4;
+    const int n = blockIdx.z / nCB;
+    const int c0 = (blockIdx.z - n * nCB) * 16;
+    const int h0 = blockIdx.y * kTileRows;
+    const int w0 = blockIdx.x * kTileCols;
+    const int64_t HW = (int64_t)H * W;
+    const bool aligned4 = al != 0;
+    const bool cvec = Elem<T>::is_bf16 ? (al != 0 && (C & 7) == 0) : (al != 0 && (C & 3) == 0);
+
+    const T *__restrict__ xn = x + (int64_t)n * C * HW;
+    const T *__restrict__ yn = y + (int64_t)n * C * HW;
+    stage_x_tile<T, K>(xs, xn, c0, C, H, W, HW, h0, w0);
+
+    const int h = h0 + wave;
+    const bool row_ok = h < H;
+    const int w = w0 + 4 * j;
+    const int64_t rowoff = (int64_t)h * W;
+    const int nq = (C + G::CH - 1) / G::CH;
+
+    typename G::BFrag bres[KQ > 0 ? KQ : 1];
+    if constexpr (KQ > 0) {
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) bres[q] = G::load_B(yn, q, g, C, HW, rowoff, w, W, row_ok, aligned4);
+    }
+    __syncthreads();
+
+    const int cA = c0 + j;  // channel of the generator row this lane supplies
+    float oacc[3][4][4];    // [branch][v][pb]
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) oacc[b][v][pb] = 0.f;
+
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+        const int D = dilation(b);
+#pragma unroll 1
+        for (int t = 0; t < KK; ++t) {
+            const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
+            float bias[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int c = c0 + 4 * g + v;
+                bias[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+            }
+            f32x4 acc[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
+            if constexpr (KQ > 0) {
+#pragma unroll
+                for (int q = 0; q < KQ; ++q) G::mma(acc, G::load_A(arow, q, g, C, cvec), bres[q]);
+            } else {
+                for (int q = 0; q < nq; ++q)
+                    G::mma(acc, G::load_A(arow, q, g, C, cvec),
+                           G::load_B(yn, q, g, C, HW, rowoff, w, W, row_ok, aligned4));
+            }
+            const int ki = t / K;
+            const int kj = t - ki * K;
+            const float *xl = xs + (wave + X::HALO + (ki - r) * D) * X::LW + 4 * j + X::HALO + (kj - r) * D;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float *xr = xl + (4 * g + v) * X::PLANE;
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) oacc[b][v][pb] += Elem<T>::quant(acc[pb][v]) * xr[pb];
+            }
+        }
+    }
+
+    if (!row_ok) return;
+    T *__restrict__ on = out + (int64_t)n * 4 * C * HW;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int c = c0 + 4 * g + v;
+        if (c >= C) continue;
+        copy4_row(xn + (int64_t)c * HW + rowoff, on + (int64_t)c * HW + rowoff, w, W, aligned4);
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+            store4_row(on + (int64_t)((1 + b) * C + c) * HW + rowoff, w, W,
+                       f32x4{oacc[b][v][0], oacc[b][v][1], oacc[b][v][2], oacc[b][v][3]}, aligned4);
+    }
+}
+
+template <typename T, int K, int KQ>
+static hipError_t launch_fused_t(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
+                                 int C, int H, int W, bool al, hipStream_t stream) {
+    auto kern = fused_fwd_kernel<T, K, KQ>;
+    const size_t lds = XTile<K>::bytes;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((W + kTileCols - 1) / kTileCols, (H + kTileRows - 1) / kTileRows, N * ((C + 15) / 16));
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, (const T *)x, (const T *)y, (const T *)wg,
+                       (const T *)bg, (T *)out, C, H, W, al ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <typename T, int K>
+static hipError_t launch_fused_k(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
+                                 int C, int H, int W, bool al, hipStream_t stream) {
+    const int nq = (C + Gen<T>::CH - 1) / Gen<T>::CH;
+    if constexpr (Elem<T>::is_bf16) {
+        if (nq == 1) return launch_fused_t<T, K, 1>(x, y, wg, bg, out, N, C, H, W, al, stream);
+        if (nq == 2) return launch_fused_t<T, K, 2>(x, y, wg, bg, out, N, C, H, W, al, stream);
+    } else {
+        if (nq == 1) return launch_fused_t<T, K, 1>(x, y, wg, bg, out, N, C, H, W, al, stream);
+        if (nq == 2) return launch_fused_t<T, K, 2>(x, y, wg, bg, out, N, C, H, W, al, stream);
+        if (nq <= 4) return launch_fused_t<T, K, 4>(x, y, wg, bg, out, N, C, H, W, al, stream);
+    }
+    return launch_fused_t<T, K, 0>(x, y, wg, bg, out, N, C, H, W, al, stream);
+}
+
+hipError_t launch_fused_fwd(const void *x, const void *y, const void *wg, const void *bg, void *out, int N, int C,
+                            int H, int W, int K, bool bf16, bool al, hipStream_t stream) {
+    if (bf16) {
+        switch (K) {
+            case 1: return launch_fused_k<bf16_t, 1>(x, y, wg, bg, out, N, C, H, W, al, stream);
+            case 3: return launch_fused_k<bf16_t, 3>(x, y, wg, bg, out, N, C, H, W, al, stream);
+            default: return launch_fused_k<bf16_t, 5>(x, y, wg, bg, out, N, C, H, W, al, stream);
+        }
+    }
+    switch (K) {
+        case 1: return launch_fused_k<float, 1>(x, y, wg, bg, out, N, C, H, W, al, stream);
+        case 3: return launch_fused_k<float, 3>(x, y, wg, bg, out, N, C, H, W, al, stream);
+        default: return launch_fused_k<float, 5>(x, y, wg, bg, out, N, C, H, W, al, stream);
+    }
+}
+
+}  // namespace ddpm

@@ -1,0 +1,26 @@
+// launchers.hpp -- internal host launchers behind the C ABI (not exported).
+// Arguments are validated by the ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ddpm {
+
+// `vec`: pixels per thread for the materialised filter (W % vec == 0 and the
+// pointers aligned to vec elements), chosen by the ABI layer.
+hipError_t launch_filter_fwd(const void *x, const void *taps, void *out, int N, int C, int H, int W, int K,
+                             bool bf16, int vec, hipStream_t stream);
+
+// `aligned4`: W % 4 == 0 and every tensor pointer 16-byte aligned.
+hipError_t launch_fused_fwd(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
+                            int C, int H, int W, int K, bool bf16, bool aligned4, hipStream_t stream);
+
+// gx, gy or (dw_part, db_part) may be null: that part is skipped.
+hipError_t launch_fused_bwd(const void *x, const void *y, const void *wg, const void *bg, const void *gout,
+                            void *gx, void *gy, float *dw_part, float *db_part, int S, int N, int C, int H,
+                            int W, int K, bool bf16, bool aligned4, hipStream_t stream);
+
+hipError_t launch_reduce_partials(const float *dw_part, const float *db_part, int S, void *gw, void *gb,
+                                  int64_t R, int C, bool bf16, hipStream_t stream);
+
+}  // namespace ddpm

@@ -1,0 +1,155 @@
+/*
+ * ddpm.h -- C ABI of the MI355X (gfx950) library for the Dynamic Dilated Pyramid
+ * Module (DDPM) of HDFNet (ECCV 2020).
+ *
+ * The operation (page "lartpang/DynamicConvolutionOperator", sections
+ * "问题与目标" / problem and goal, "CUDA 动态过滤" / dynamic filter,
+ * "CUDA 融合生成器推理" / fused generator inference and "CUDA Flash 式融合训练" /
+ * flash-style fused training):
+ *
+ *   A 1x1 generator over guidance features y produces, at every pixel, K*K
+ *   depthwise taps per channel for each of the dilations D = (1, 3, 5):
+ *       T[n, o, p] = bias[o] + sum_c' weight[o, c'] * y[n, c', p]
+ *   with generator channel o = (b*C + c)*K*K + t, branch b for dilation D_b,
+ *   tap t = ki*K + kj.  Branch b of channel c at pixel p = (h, w) is
+ *       O_b[n, c, h, w] = sum_t T[n, o, h, w] * x[n, c, h + (ki-r)*D_b, w + (kj-r)*D_b]
+ *   with r = (K-1)/2 and x read as zero outside the image (zero padding
+ *   D_b*r, stride 1).  The output is the concatenation [x, O_0, O_1, O_2]
+ *   along channels, shape [N, 4C, H, W].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer is a DEVICE pointer to contiguous row-major memory
+ *   owned by the caller: x, y, grad_x, grad_y are [N, C, H, W]; weight is
+ *   [3*C*K*K, C]; bias is [3*C*K*K]; taps is [N, 3*C*K*K, H, W]; out and
+ *   grad_out are [N, 4*C, H, W].  Tensors are in `dtype` unless stated; the
+ *   weight-gradient partials are always float32.  The library never allocates,
+ *   frees or synchronises; it keeps no state between calls.  Outputs must not
+ *   overlap inputs or each other.  Every output element is written exactly once
+ *   (nothing is accumulated into), so outputs need no zeroing.
+ * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
+ *   returns without waiting; faults inside kernels surface at the caller's next
+ *   synchronisation.
+ * Precision (page section "CUDA Flash 式融合训练", precision policy).  All sums
+ *   are accumulated in float32.  float32 calls use full float32 matrix
+ *   arithmetic (no reduced-precision operands).  bfloat16 calls round each
+ *   generated tap to bfloat16 (round-to-nearest-even) before it is used, round
+ *   each formed dK value to bfloat16 where it feeds a matrix product, and round
+ *   every bfloat16 output once at the end.  The x block of `out` is a bit-exact
+ *   copy of x.
+ * Errors.  Every function validates all arguments before it enqueues anything;
+ *   a call that fails validation writes nothing.
+ *     DDPM_ERR_INVALID_ARG  a null pointer, N, C, H or W < 1, H*W >= 2^31,
+ *                           C > DDPM_MAX_C, an unknown dtype, or
+ *                           num_partials outside [1, DDPM_MAX_PARTIALS];
+ *     DDPM_ERR_UNSUPPORTED  K not in {1, 3, 5} (the dilation set is fixed);
+ *     DDPM_ERR_HIP          a HIP launch or attribute call failed.
+ *   No C++ exception crosses this interface.  Calls are re-entrant and
+ *   thread-safe.
+ */
+#ifndef DDPM_H_
+#define DDPM_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DDPM_F32 = 0, DDPM_BF16 = 1 } ddpm_dtype;
+
+typedef enum {
+    DDPM_OK = 0,
+    DDPM_ERR_INVALID_ARG = -1,
+    DDPM_ERR_UNSUPPORTED = -2,
+    DDPM_ERR_HIP = -3
+} ddpm_status;
+
+/* Largest depthwise channel count accepted. */
+#define DDPM_MAX_C 1024
+/* Largest number of float32 weight-gradient partials (page section
+ * "CUDA Flash 式融合训练": tokens are split into at most 16 fp32 partials). */
+#define DDPM_MAX_PARTIALS 16
+
+/*
+ * ddpm_filter_fwd -- dynamic dilated filter with materialised taps
+ * (page section "CUDA 动态过滤": one pass serves dilations 1, 3 and 5 from one
+ * spatial tile, float32 accumulation, output written directly as [x, d1, d3, d5]).
+ *
+ *   x    [N, C, H, W]            in   dtype
+ *   taps [N, 3*C*K*K, H, W]      in   dtype, generator channel order as above
+ *   out  [N, 4*C, H, W]          out  dtype
+ *
+ * Returns DDPM_OK or an error code from the list above.
+ */
+int ddpm_filter_fwd(const void *x, const void *taps, void *out,
+                    int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype,
+                    hipStream_t stream);
+
+/*
+ * ddpm_fused_fwd -- generator fused with the filter (page section
+ * "CUDA 融合生成器推理": weight x y-tile -> taps -> consumed with shifted x; the
+ * taps never reach global memory).
+ *
+ *   x, y    [N, C, H, W]         in   dtype
+ *   weight  [3*C*K*K, C]         in   dtype
+ *   bias    [3*C*K*K]            in   dtype
+ *   out     [N, 4*C, H, W]       out  dtype
+ */
+int ddpm_fused_fwd(const void *x, const void *y, const void *weight, const void *bias,
+                   void *out, int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype,
+                   hipStream_t stream);
+
+/*
+ * ddpm_fused_bwd -- training backward with tap recompute (page section
+ * "CUDA Flash 式融合训练"): dX recomputes the taps and gathers each dilation's
+ * contribution; dY forms dK = shifted(x) * grad on chip and contracts it with
+ * the generator weight; dWeight / dbias form dK on chip and reduce it over
+ * space into float32 partials, one per contiguous token range.
+ *
+ *   x, y, weight, bias     in   as for ddpm_fused_fwd
+ *   grad_out [N, 4*C, H, W]           in   dtype (dL/d out)
+ *   grad_x   [N, C, H, W]             out  dtype (includes the x-block passthrough)
+ *   grad_y   [N, C, H, W]             out  dtype
+ *   dweight_partials [num_partials, 3*C*K*K, C]   out  float32
+ *   dbias_partials   [num_partials, 3*C*K*K]      out  float32
+ *   num_partials in [1, DDPM_MAX_PARTIALS]: the N*H*W tokens, in (n, h, w)
+ *   order, are cut into num_partials contiguous ranges whose lengths differ by
+ *   at most one; partial s holds the sum over range s.  Reduce them with
+ *   ddpm_reduce_partials.
+ *   Optional outputs: grad_x may be NULL (dX is not computed), grad_y may be
+ *   NULL (dY is not computed), and dweight_partials / dbias_partials may both be
+ *   NULL (dWeight / dbias are not computed; then num_partials is ignored).  At
+ *   least one of the three must be requested, and the two partial pointers must
+ *   be both NULL or both non-NULL; otherwise DDPM_ERR_INVALID_ARG.  Each part
+ *   runs as its own kernel, so requesting a subset does only that work.
+ */
+int ddpm_fused_bwd(const void *x, const void *y, const void *weight, const void *bias,
+                   const void *grad_out, void *grad_x, void *grad_y,
+                   float *dweight_partials, float *dbias_partials, int num_partials,
+                   int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype,
+                   hipStream_t stream);
+
+/*
+ * ddpm_reduce_partials -- the short second kernel of the split reduction
+ * (page section "CUDA Flash 式融合训练"): sums the partials in ascending split
+ * order in float32 and writes the gradients in `dtype`.
+ *
+ *   dweight_partials [num_partials, 3*C*K*K, C]  in   float32
+ *   dbias_partials   [num_partials, 3*C*K*K]     in   float32
+ *   grad_weight      [3*C*K*K, C]                out  dtype
+ *   grad_bias        [3*C*K*K]                   out  dtype
+ */
+int ddpm_reduce_partials(const float *dweight_partials, const float *dbias_partials,
+                         int num_partials, void *grad_weight, void *grad_bias,
+                         int64_t C, int K, int dtype, hipStream_t stream);
+
+/* Static, human-readable name of a ddpm_status value. */
+const char *ddpm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDPM_H_ */

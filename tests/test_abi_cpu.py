@@ -1,0 +1,146 @@
+"""C-ABI contract checks that need no GPU.
+
+* The library loads and exports every function that ``include/ddpm.h`` declares.
+* Argument validation rejects bad calls with the documented status before anything
+  is enqueued: every call below fails validation, so no HIP runtime call is made
+  (the library touches the runtime only after validation succeeds).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_dilated_depthwise_amd as ddpm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddpm.h")
+
+OK, INVALID, UNSUPPORTED, HIPERR = 0, -1, -2, -3
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ddpm.library_path()):
+        from dynamic_dilated_depthwise_amd import build
+        build.build(verbose=False)
+    return ddpm.raw_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddpm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "ddpm_filter_fwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials", "ddpm_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libddpm.so does not export {name}"
+
+
+def test_status_strings(lib):
+    assert ddpm.ddpm_status_string(OK) == "DDPM_OK"
+    assert ddpm.ddpm_status_string(INVALID) == "DDPM_ERR_INVALID_ARG"
+    assert ddpm.ddpm_status_string(UNSUPPORTED) == "DDPM_ERR_UNSUPPORTED"
+    assert ddpm.ddpm_status_string(HIPERR) == "DDPM_ERR_HIP"
+
+
+# Fake, well-aligned, non-overlapping "device" addresses; never dereferenced because
+# every call below fails validation first.
+A = 1 << 40
+B = 2 << 40
+Cp = 3 << 40
+D = 4 << 40
+E = 5 << 40
+F = 6 << 40
+G = 7 << 40
+Hp = 8 << 40
+Ip = 9 << 40
+
+
+def _filter(lib, x=A, taps=B, out=Cp, N=1, C=8, H=16, W=16, K=3, dt=F32):
+    return lib.ddpm_filter_fwd(x, taps, out, N, C, H, W, K, dt, None)
+
+
+def _fused(lib, x=A, y=B, w=Cp, b=D, out=E, N=1, C=8, H=16, W=16, K=3, dt=F32):
+    return lib.ddpm_fused_fwd(x, y, w, b, out, N, C, H, W, K, dt, None)
+
+
+def _bwd(lib, x=A, y=B, w=Cp, b=D, g=E, gx=F, gy=G, pw=Hp, pb=Ip, S=1, N=1, C=8, H=16, W=16, K=3, dt=F32):
+    return lib.ddpm_fused_bwd(x, y, w, b, g, gx, gy, pw, pb, S, N, C, H, W, K, dt, None)
+
+
+def _reduce(lib, pw=A, pb=B, S=1, gw=Cp, gb=D, C=8, K=3, dt=F32):
+    return lib.ddpm_reduce_partials(pw, pb, S, gw, gb, C, K, dt, None)
+
+
+@pytest.mark.parametrize("call", [_filter, _fused, _bwd])
+def test_shape_validation(lib, call):
+    for kw in (dict(N=0), dict(C=0), dict(H=0), dict(W=-1), dict(C=4096), dict(dt=2), dict(dt=-1),
+               dict(H=1 << 16, W=1 << 15)):
+        assert call(lib, **kw) == INVALID, kw
+    for K in (0, 2, 4, 7, -3):
+        assert call(lib, K=K) == UNSUPPORTED, K
+
+
+def test_null_and_misaligned_pointers(lib):
+    for name in ("x", "taps", "out"):
+        assert _filter(lib, **{name: 0}) == INVALID
+    assert _filter(lib, x=A + 2) == INVALID              # float32 needs 4-byte alignment
+    assert _filter(lib, x=A + 1, dt=BF16) == INVALID     # bfloat16 needs 2-byte alignment
+    for name in ("x", "y", "w", "b", "out"):
+        assert _fused(lib, **{name: 0}) == INVALID
+    for name in ("x", "y", "w", "b", "g", "pw", "pb"):
+        assert _bwd(lib, **{name: 0}) == INVALID       # pw / pb alone: both or neither
+    assert _bwd(lib, gx=0, gy=0, pw=0, pb=0) == INVALID  # nothing requested
+    assert _bwd(lib, pw=Hp + 2, dt=BF16) == INVALID      # partials are float32 in every dtype
+    for name in ("pw", "pb", "gw", "gb"):
+        assert _reduce(lib, **{name: 0}) == INVALID
+
+
+def test_partial_count_validation(lib):
+    for S in (0, -1, 17, 1000):
+        assert _bwd(lib, S=S) == INVALID
+        assert _reduce(lib, S=S) == INVALID
+        # with no partials requested the count is not used (checked on a call
+        # that still fails validation, so nothing is launched)
+        assert _bwd(lib, S=S, pw=0, pb=0, K=2) == UNSUPPORTED
+
+
+def test_reduce_shape_validation(lib):
+    assert _reduce(lib, C=0) == INVALID
+    assert _reduce(lib, dt=3) == INVALID
+    assert _reduce(lib, K=2) == UNSUPPORTED
+
+
+def test_overlapping_outputs_rejected(lib):
+    assert _filter(lib, out=A) == INVALID
+    assert _filter(lib, out=B + 64) == INVALID
+    assert _fused(lib, out=B) == INVALID
+    assert _bwd(lib, gx=A) == INVALID
+    assert _bwd(lib, gy=F) == INVALID
+    assert _bwd(lib, pb=Hp) == INVALID
+    assert _reduce(lib, gw=A) == INVALID
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 8, 4, 4)
+    taps = torch.zeros(1, 3 * 8 * 9, 4, 4)
+    out = torch.zeros(1, 32, 4, 4)
+    with pytest.raises(ValueError):
+        ddpm.ddpm_filter_fwd(x, taps, out, 3)
+
+
+def test_num_partials_policy():
+    assert ddpm.num_partials_for(1, 16, 16) == 1
+    assert ddpm.num_partials_for(2, 15, 17) == 1
+    assert ddpm.num_partials_for(1, 128, 128) == 16
+    assert ddpm.num_partials_for(1, 256, 256) == 16
+    assert ddpm.num_partials_for(1, 40, 40) == 2

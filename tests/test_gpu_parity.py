@@ -1,0 +1,196 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Every case draws seeded inputs (``dynamic_dilated_depthwise_amd.synth``), runs the
+library through its C ABI (via the thin binding) on the GPU and the oracle on the
+host on exactly the same values, and compares whole tensors:
+  * the named workloads at their full sizes (1x64x128^2 K=3 filter, 1x64x256^2
+    K=3 fused forward / backward, 1x64x128^2 K=5 training) in the launch
+    configuration the benchmark times;
+  * small and ragged shapes that span several tiles with partial tiles at the
+    right and bottom edges, K = 1, 3, 5, images smaller than the dilation reach,
+    channel counts that are not multiples of the MFMA block, more than 64
+    channels (the streamed generator path), the largest channel count, and
+    tensors whose pointers are only element-aligned.
+Tolerances are in ``gpu_cases.py``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_dilated_depthwise_amd as ddpm
+from dynamic_dilated_depthwise_amd import synth
+from gpu_cases import (TOL, announce, assert_close, dev, f64, gpu_bwd, gpu_filter, gpu_fused, inputs, orc)
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+S_ = synth.Shape
+
+FWD_CASES = [
+    ("tiny", None), ("nonaligned", None), ("bw_filter_128", None), ("fused_inference_256", None),
+    ("fused_training_128_k5", None),
+    ("k1", (S_(1, 8, 16, 16, 1), 101)), ("k5", (S_(1, 8, 16, 16, 5), 102)),
+    ("nonaligned_k5", (S_(2, 24, 15, 17, 5), 103)), ("nonaligned_k1", (S_(2, 24, 15, 17, 1), 104)),
+    ("one_pixel", (S_(1, 1, 1, 1, 3), 105)), ("one_row_k5", (S_(1, 3, 1, 7, 5), 106)),
+    ("smaller_than_reach", (S_(1, 5, 3, 3, 3), 107)), ("ragged_tiles", (S_(3, 16, 9, 65, 3), 108)),
+    ("c33", (S_(1, 33, 10, 8, 3), 109)), ("c70_streamed", (S_(1, 70, 12, 20, 3), 110)),
+    ("c1024_max", (S_(1, 1024, 2, 2, 3), 111)), ("c2_k5_tall", (S_(2, 2, 37, 6, 5), 112)),
+]
+
+BWD_CASES = [
+    ("tiny", None), ("nonaligned", None), ("fused_training_128_k5", None), ("target_256", None),
+    ("k1", (S_(1, 8, 16, 16, 1), 201)), ("k5", (S_(1, 8, 16, 16, 5), 202)),
+    ("nonaligned_k5", (S_(2, 24, 15, 17, 5), 203)),
+    ("one_pixel", (S_(1, 1, 1, 1, 3), 205)), ("smaller_than_reach", (S_(1, 5, 3, 3, 3), 207)),
+    ("ragged_tiles", (S_(3, 16, 9, 65, 3), 208)), ("c33", (S_(1, 33, 10, 8, 3), 209)),
+    ("c70_streamed", (S_(1, 70, 12, 20, 3), 210)), ("c2_k5_tall", (S_(2, 2, 37, 6, 5), 212)),
+]
+
+
+def _resolve(name, spec):
+    return synth.WORKLOADS[name] if spec is None else spec
+
+
+_ref_cache = {}
+
+
+def _fwd_ref(key, a, K, taps):
+    if key not in _ref_cache:
+        o = orc()
+        if taps:
+            _ref_cache[key] = o.filter_fwd(a["x"], a["taps"], K)
+        else:
+            _ref_cache[key] = o.fused_fwd(a["x"], a["y"], a["weight"], a["bias"], K)
+    return _ref_cache[key]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name,spec", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_filter_fwd(name, spec, dt):
+    shape, block = _resolve(name, spec)
+    dtype = DT[dt]
+    h = inputs(shape, block, dtype, taps=True)
+    a = {k: f64(v) for k, v in h.items()}
+    ref = _fwd_ref(("filter", name, dt), a, shape.K, taps=True)
+    announce("filter_fwd", name, dt, shape)
+    d = dev(h)
+    out = gpu_filter(d, shape.K)
+    C = shape.C
+    assert torch.equal(out[:, :C].cpu().view(torch.int16 if dt == "bf16" else torch.int32),
+                       h["x"].view(torch.int16 if dt == "bf16" else torch.int32)), "x block not bit-exact"
+    assert_close(f64(out), ref, TOL[dtype]["out"], f"filter {name} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name,spec", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_fused_fwd(name, spec, dt):
+    shape, block = _resolve(name, spec)
+    dtype = DT[dt]
+    h = inputs(shape, block, dtype)
+    a = {k: f64(v) for k, v in h.items()}
+    ref = _fwd_ref(("fused", name, dt), a, shape.K, taps=False)
+    announce("fused_fwd", name, dt, shape)
+    out = gpu_fused(dev(h), shape.K)
+    C = shape.C
+    assert torch.equal(out[:, :C].cpu(), h["x"]), "x block not bit-exact"
+    assert_close(f64(out), ref, TOL[dtype]["out"], f"fused {name} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name,spec", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_fused_bwd(name, spec, dt):
+    shape, block = _resolve(name, spec)
+    dtype = DT[dt]
+    h = inputs(shape, block, dtype, grad=True)
+    a = {k: f64(v) for k, v in h.items()}
+    refs = orc().fused_bwd(a["x"], a["y"], a["weight"], a["bias"], a["grad_out"], shape.K)
+    announce("fused_bwd", name, dt, shape)
+    gx, gy, gw, gb, _, _ = gpu_bwd(dev(h), shape.K)
+    tol = TOL[dtype]["grad"]
+    for what, got, ref in zip(("dx", "dy", "dweight", "dbias"), (gx, gy, gw, gb), refs):
+        assert_close(f64(got), ref, tol, f"{what} {name} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_misaligned_pointers(dt):
+    """Element-aligned (not 16-byte aligned) tensors take the scalar/unaligned paths."""
+    dtype = DT[dt]
+    shape = S_(2, 24, 15, 16, 3)
+    h = inputs(shape, 301, dtype, taps=True, grad=True)
+    a = {k: f64(v) for k, v in h.items()}
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, device="cuda", dtype=t.dtype)
+        v = buf[1:].view(t.shape)
+        v.copy_(t.to("cuda"))
+        return v
+
+    d = {k: shifted(v) for k, v in h.items()}
+    assert d["x"].data_ptr() % 16 != 0
+    announce("misaligned", dt, shape)
+    o = orc()
+    K = shape.K
+    assert_close(f64(gpu_filter(d, K)), o.filter_fwd(a["x"], a["taps"], K), TOL[dtype]["out"], "filter")
+    assert_close(f64(gpu_fused(d, K)), o.fused_fwd(a["x"], a["y"], a["weight"], a["bias"], K),
+                 TOL[dtype]["out"], "fused")
+    refs = o.fused_bwd(a["x"], a["y"], a["weight"], a["bias"], a["grad_out"], K)
+    got = gpu_bwd(d, K)[:4]
+    for what, g_, r_ in zip(("dx", "dy", "dweight", "dbias"), got, refs):
+        assert_close(f64(g_), r_, TOL[dtype]["grad"], what)
+
+
+@pytest.mark.parametrize("S", [1, 3, 7, 16])
+def test_partial_counts_agree(S):
+    """Any split count gives the same reduced gradients (within float32 rounding)."""
+    shape = S_(2, 24, 15, 17, 3)
+    h = inputs(shape, 302, torch.float32, grad=True)
+    a = {k: f64(v) for k, v in h.items()}
+    _, _, dW, db = orc().fused_bwd(a["x"], a["y"], a["weight"], a["bias"], a["grad_out"], shape.K)
+    announce("partials", S, shape)
+    _, _, gw, gb, pw, pb = gpu_bwd(dev(h), shape.K, S=S)
+    assert_close(f64(gw), dW, 1e-3, f"dweight S={S}")
+    assert_close(f64(gb), db, 1e-3, f"dbias S={S}")
+    # the reduce kernel is an ascending-order fp32 sum of the partials
+    ref = pw.cpu().double().sum(0).numpy()
+    assert_close(f64(gw), ref, 1e-6, "reduce of partials")
+
+
+@pytest.mark.parametrize("name", ["nonaligned", "fused_training_128_k5"])
+def test_bitwise_deterministic(name):
+    shape, block = synth.WORKLOADS[name]
+    d = dev(inputs(shape, block, torch.float32, grad=True, taps=True))
+    announce("determinism", name)
+    r1 = (gpu_filter(d, shape.K), gpu_fused(d, shape.K), *gpu_bwd(d, shape.K))
+    r2 = (gpu_filter(d, shape.K), gpu_fused(d, shape.K), *gpu_bwd(d, shape.K))
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
+
+
+def test_finite_difference_spot_check():
+    """<grad, v> from the GPU backward equals the central difference of
+    L = <G, out> evaluated from GPU forwards; exact in exact arithmetic because L
+    is affine in each of x, y, weight, bias taken alone."""
+    shape, block = synth.WORKLOADS["nonaligned"]
+    h = inputs(shape, block, torch.float32, grad=True)
+    d = dev(h)
+    K = shape.K
+    announce("fd", shape)
+    gx, gy, gw, gb, _, _ = gpu_bwd(d, K)
+    grads = {"x": gx, "y": gy, "weight": gw, "bias": gb}
+    G = f64(d["grad_out"])
+    gen = torch.Generator().manual_seed(7)
+    for name in ("x", "y", "weight", "bias"):
+        v = torch.randn(d[name].shape, generator=gen).to("cuda")
+        eps = 0.25
+        dp = dict(d, **{name: (d[name] + eps * v).contiguous()})
+        dm = dict(d, **{name: (d[name] - eps * v).contiguous()})
+        Lp = float((f64(gpu_fused(dp, K)) * G).sum())
+        Lm = float((f64(gpu_fused(dm, K)) * G).sum())
+        fd = (Lp - Lm) / (2 * eps)
+        gv = f64(grads[name])
+        vv = f64(v)
+        an = float((gv * vv).sum())
+        # Cauchy-Schwarz scale of <grad, v>; float32 rounding in the forward keeps
+        # |fd - an| far below 2e-5 of it, while a wrong or missing term does not.
+        scale = float(np.linalg.norm(gv) * np.linalg.norm(vv))
+        assert abs(fd - an) <= 2e-5 * scale + 5e-3, f"FD {name}: {fd} vs {an} (scale {scale:.3g})"
