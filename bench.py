@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--workload", default="target_256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, time a plain device-to-device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM counters, and the attainable-bandwidth ceiling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,6 +149,25 @@ def main():
             fn()
             if events is not None:
                 events[i][1].record(stream)
+
+    copy_cal = None
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        copy_cal = {"bytes_read": nbytes, "bytes_written": nbytes, "median_ms": round(ms, 5),
+                    "GB_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+        log(f"copy calibration {copy_cal}")
+        del src, dst
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -236,6 +258,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if copy_cal is not None:
+        line["copy_calibration"] = copy_cal
     print(json.dumps(line), flush=True)
 
 

@@ -106,6 +106,65 @@ __device__ __forceinline__ f32x4 load4_row(const T *__restrict__ row, int w, int
     return v;
 }
 
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint16_t u16x8_a16 __attribute__((ext_vector_type(8), aligned(16)));
+
+// Eight consecutive bf16 pixels w..w+7 of one row, widened to float; zero outside
+// [0, W) or when !row_ok.  Uses one 16-byte load when the address allows it, else
+// dword loads (realigned in registers), else element loads at the row ends.
+__device__ __forceinline__ void load8_bf16_row(const bf16_t *__restrict__ row, int w, int W, bool row_ok,
+                                               float (&v)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    if (!row_ok) return;
+    const uintptr_t a = (uintptr_t)(row + w);
+    if (w >= 0 && w + 7 < W && ((a & 3) == 0 || w >= 1)) {
+        if ((a & 15) == 0) {
+            const u16x8 u = *(const u16x8_a16 *)(row + w);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = bf16_bits_to_f32(u[k]);
+        } else if ((a & 3) == 0) {
+            const u32x4_a4 d = *(const u32x4_a4 *)(row + w);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = __uint_as_float(d[k] << 16);
+                v[2 * k + 1] = __uint_as_float(d[k] & 0xffff0000u);
+            }
+        } else {
+            // row + w - 1 is 4-byte aligned and w - 1 >= 0 lies in this row.
+            const u32x4_a4 d = *(const u32x4_a4 *)(row + w - 1);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = __uint_as_float(d[k] & 0xffff0000u);
+                if (k < 3) v[2 * k + 1] = __uint_as_float(d[k + 1] << 16);
+            }
+            v[7] = bf16_bits_to_f32(row[w + 7]);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int ww = w + k;
+            if (ww >= 0 && ww < W) v[k] = bf16_bits_to_f32(row[ww]);
+        }
+    }
+}
+
+// RL consecutive pixels of a row as float: 4 for float32 tensors, 8 for bf16.
+template <typename T, int RL> struct RowRun;
+template <> struct RowRun<float, 4> {
+    __device__ __forceinline__ static void load(const float *__restrict__ row, int w, int W, bool ok, bool al,
+                                                float (&v)[4]) {
+        const f32x4 t = load4_row(row, w, W, ok, al && ((w & 3) == 0));
+        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    }
+};
+template <> struct RowRun<bf16_t, 8> {
+    __device__ __forceinline__ static void load(const bf16_t *__restrict__ row, int w, int W, bool ok, bool,
+                                                float (&v)[8]) {
+        load8_bf16_row(row, w, W, ok, v);
+    }
+};
+
 // Raw (bit-exact) copy helpers for the x block of the output.
 template <typename T>
 __device__ __forceinline__ void copy4_row(const T *__restrict__ src, T *__restrict__ dst, int w, int W,

@@ -56,49 +56,78 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) dacc[v][pb] = 0.f;
 
+    // Operands of one (tap, channel chunk) step: a generator-row fragment and y at
+    // the tap's shifted pixels.  The loop runs over (tap t, chunk q) steps with the
+    // next step's loads issued before the current step's MFMAs.
+    struct Step {
+        typename G::AFrag a;
+        typename G::BFrag y;
+    };
+    const int nsteps_q = nq;
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
         const int D = dilation(b);
+        auto fetch = [&](int t, int q, Step &st) {
+            const int ki = t / K;
+            const int kj = t - ki * K;
+            const int hs = h - (ki - r) * D;
+            const int dc = (kj - r) * D;
+            const bool rs_ok = hs >= 0 && hs < H;
+            const int64_t rowoff = (int64_t)(rs_ok ? hs : 0) * W;
+            const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
+            st.a = G::load_A(arow, q, g, C, cvec);
+            st.y = G::load_B(yn, q, g, C, HW, rowoff, w - dc, W, rs_ok, aligned4 && ((dc & 3) == 0));
+        };
+        Step cur;
+        fetch(0, 0, cur);
 #pragma unroll 1
         for (int t = 0; t < KK; ++t) {
             const int ki = t / K;
             const int kj = t - ki * K;
-            const int dr = (ki - r) * D;
-            const int dc = (kj - r) * D;
-            const int hs = h - dr;
-            const int ws = w - dc;
+            const int hs = h - (ki - r) * D;
+            const int ws = w - (kj - r) * D;
             const bool rs_ok = hs >= 0 && hs < H;
-            const bool al_s = aligned4 && ((dc & 3) == 0);
+            const bool al_s = aligned4 && ((((kj - r) * D) & 3) == 0);
             const int64_t rowoff = (int64_t)(rs_ok ? hs : 0) * W;
-
-            const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
             float bias[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int c = c0 + 4 * g + v;
                 bias[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
             }
-            f32x4 acc[4];
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
-#pragma unroll
-            for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) {
-                if (KQ > 0 || q < nq) {
-                    G::mma(acc, G::load_A(arow, q, g, C, cvec), G::load_B(yn, q, g, C, HW, rowoff, ws, W, rs_ok, al_s));
-                }
-            }
-            if constexpr (KQ == 0) {
-                for (int q = 1; q < nq; ++q)
-                    G::mma(acc, G::load_A(arow, q, g, C, cvec), G::load_B(yn, q, g, C, HW, rowoff, ws, W, rs_ok, al_s));
-            }
+            // G_b at the source pixels (consumed after the MFMAs)
+            f32x4 gs[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int c = c0 + 4 * g + v;
-                const f32x4 gs = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, ws, W,
-                                           rs_ok && c < C, al_s);
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += Elem<T>::quant(acc[pb][v]) * gs[pb];
+                gs[v] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, ws, W, rs_ok && c < C,
+                                  al_s);
             }
+            f32x4 acc[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
+            if constexpr (KQ > 0) {
+#pragma unroll
+                for (int q = 0; q < KQ; ++q) {
+                    Step nxt;
+                    if (q + 1 < KQ) fetch(t, q + 1, nxt);
+                    else if (t + 1 < KK) fetch(t + 1, 0, nxt);
+                    G::mma(acc, cur.a, cur.y);
+                    cur = nxt;
+                }
+            } else {
+                for (int q = 0; q < nsteps_q; ++q) {
+                    Step nxt;
+                    if (q + 1 < nsteps_q) fetch(t, q + 1, nxt);
+                    else if (t + 1 < KK) fetch(t + 1, 0, nxt);
+                    G::mma(acc, cur.a, cur.y);
+                    cur = nxt;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += Elem<T>::quant(acc[pb][v]) * gs[v][pb];
         }
     }
 
@@ -164,23 +193,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
                 const bool c_ok = c < C;
                 const f32x4 gb = load4_row(gn + (int64_t)((1 + b) * C + (c_ok ? c : 0)) * HW + rowoff, w, W, c_ok,
                                            aligned4);
-#pragma unroll 1
-                for (int t = 0; t < KK; ++t) {
+                // x at the tap's shifted pixels and the weight column fragments of
+                // tap t, fetched one tap ahead of their MFMAs.
+                auto fetch = [&](int t, f32x4 &xs, float (&a)[MB]) {
                     const int ki = t / K;
                     const int kj = t - ki * K;
                     const int hh = h + (ki - r) * D;
                     const int dc = (kj - r) * D;
                     const bool rok = c_ok && hh >= 0 && hh < H;
-                    const f32x4 xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(rok ? hh : 0) * W,
-                                               w + dc, W, rok, aligned4 && ((dc & 3) == 0));
+                    xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(rok ? hh : 0) * W, w + dc, W, rok,
+                                   aligned4 && ((dc & 3) == 0));
                     const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
 #pragma unroll
                     for (int m = 0; m < MB; ++m) {
                         const int cp = cm0 + 16 * m + j;
-                        const float a = (c_ok && cp < C) ? wrow[cp] : 0.f;
-#pragma unroll
-                        for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x4_f32(a, gb[pb] * xs[pb], acc[m][pb]);
+                        a[m] = (c_ok && cp < C) ? wrow[cp] : 0.f;
                     }
+                };
+                f32x4 xn_;
+                float an_[MB];
+                fetch(0, xn_, an_);
+#pragma unroll 1
+                for (int t = 0; t < KK; ++t) {
+                    const f32x4 xs = xn_;
+                    float a[MB];
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) a[m] = an_[m];
+                    if (t + 1 < KK) fetch(t + 1, xn_, an_);
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x4_f32(a[m], gb[pb] * xs[pb], acc[m][pb]);
                 }
             } else {
                 f32x4 gb[8];
@@ -311,8 +354,21 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
         for (int nb = 0; nb < NB; ++nb) acc[cc][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int64_t p0 = t0 + (int64_t)wave * KC; p0 < t1; p0 += 4 * KC) {
-        const int64_t pf = p0 + (int64_t)g * RL;  // this lane's first token
+    // The wave walks chunks of KC tokens (t0 + wave*KC, then every 4*KC), keeping
+    // the chunk's (image, row, column) position incrementally.  A chunk that lies in
+    // one image row loads each operand as one run of RL pixels per lane; a chunk
+    // that crosses a row end or the split end takes the per-token path.
+    int64_t p0 = t0 + (int64_t)wave * KC;
+    int pn = 0, ph = 0, pw = 0;
+    if (p0 < t1) {
+        pn = (int)(p0 / HW);
+        const int64_t rem = p0 - (int64_t)pn * HW;
+        ph = (int)(rem / W);
+        pw = (int)(rem - (int64_t)ph * W);
+    }
+    const bool al = ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)gout % 16 == 0) &&
+                    (W % 4 == 0);
+    while (p0 < t1) {
         float a[CG][RL];
         float bvals[NB][RL];
 #pragma unroll
@@ -324,16 +380,47 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
 #pragma unroll
             for (int k = 0; k < RL; ++k) bvals[nb][k] = 0.f;
 
-        if (pf < t1) {
-            int n = (int)(pf / HW);
-            int64_t rem = pf - (int64_t)n * HW;
-            int hh = (int)(rem / W);
-            int ww = (int)(rem - (int64_t)hh * W);
+        if (p0 + KC <= t1 && pw + KC <= W) {
+            const int w = pw + RL * g;
+            const T *xn = x + (int64_t)pn * CHW;
+            const T *gn = gout + (int64_t)pn * 4 * CHW;
+            const T *yn = y + (int64_t)pn * CHW;
+            const int64_t rowoff = (int64_t)ph * W;
+#pragma unroll
+            for (int cc = 0; cc < CG; ++cc) {
+                const int b = cb_b[cc];
+                if (b >= 0 && cA_ok) {
+                    float gv[RL], xv[RL];
+                    RowRun<T, RL>::load(gn + (int64_t)((1 + b) * C + cA) * HW + rowoff, w, W, true, al, gv);
+                    const int hs = ph + cb_dr[cc];
+                    const bool hok = hs >= 0 && hs < H;
+                    RowRun<T, RL>::load(xn + (int64_t)cA * HW + (int64_t)(hok ? hs : 0) * W, w + cb_dc[cc], W, hok,
+                                        al, xv);
+#pragma unroll
+                    for (int k = 0; k < RL; ++k) a[cc][k] = gv[k] * xv[k];
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int cp = cn0 + 16 * nb + j;
+                if (cp < C) RowRun<T, RL>::load(yn + (int64_t)cp * HW + rowoff, w, W, true, al, bvals[nb]);
+            }
+        } else {
+            const int64_t pf = p0 + (int64_t)g * RL;  // this lane's first token
+            int n = pn, hh = ph, ww = pw + RL * g;
+            while (ww >= W) {
+                ww -= W;
+                if (++hh == H) {
+                    hh = 0;
+                    ++n;
+                }
+            }
 #pragma unroll
             for (int k = 0; k < RL; ++k) {
                 if (pf + k < t1) {
                     const T *xn = x + (int64_t)n * CHW;
                     const T *gn = gout + (int64_t)n * 4 * CHW;
+                    const T *yn = y + (int64_t)n * CHW;
                     const int64_t pix = (int64_t)hh * W + ww;
 #pragma unroll
                     for (int cc = 0; cc < CG; ++cc) {
@@ -348,7 +435,6 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
                             }
                         }
                     }
-                    const T *yn = y + (int64_t)n * CHW;
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         const int cp = cn0 + 16 * nb + j;
@@ -393,6 +479,16 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
                 const bf16x8 aq = pack_bf16x8(u);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) acc[cc][nb] = mfma_16x16x32_bf16(aq, bq[nb], acc[cc][nb]);
+            }
+        }
+        // advance to this wave's next chunk
+        p0 += 4 * KC;
+        pw += 4 * KC;
+        while (pw >= W) {
+            pw -= W;
+            if (++ph == H) {
+                ph = 0;
+                ++pn;
             }
         }
     }

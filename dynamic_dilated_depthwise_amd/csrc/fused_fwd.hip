@@ -102,22 +102,46 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
         const int D = dilation(b);
-#pragma unroll 1
-        for (int t = 0; t < KK; ++t) {
+        // Generator-row operand and bias of tap t of this branch.
+        auto fetch = [&](int t, typename G::AFrag (&af)[KQ > 0 ? KQ : 1], float (&bf)[4]) {
             const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
-            float bias[4];
+#pragma unroll
+            for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) af[q] = G::load_A(arow, q, g, C, cvec);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int c = c0 + 4 * g + v;
-                bias[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+                bf[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
             }
+        };
+        typename G::AFrag anext[KQ > 0 ? KQ : 1];
+        float bnext[4];
+        if constexpr (KQ > 0) fetch(0, anext, bnext);
+#pragma unroll 1
+        for (int t = 0; t < KK; ++t) {
             f32x4 acc[4];
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
             if constexpr (KQ > 0) {
+                // operands of tap t were fetched one tap ahead; fetch tap t+1 now
+                typename G::AFrag acur[KQ];
+                float bcur[4];
 #pragma unroll
-                for (int q = 0; q < KQ; ++q) G::mma(acc, G::load_A(arow, q, g, C, cvec), bres[q]);
+                for (int q = 0; q < KQ; ++q) acur[q] = anext[q];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) bcur[v] = bnext[v];
+                if (t + 1 < KK) fetch(t + 1, anext, bnext);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bcur[0], bcur[1], bcur[2], bcur[3]};
+#pragma unroll
+                for (int q = 0; q < KQ; ++q) G::mma(acc, acur[q], bres[q]);
             } else {
+                const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
+                float bias[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int c = c0 + 4 * g + v;
+                    bias[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+                }
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
                 for (int q = 0; q < nq; ++q)
                     G::mma(acc, G::load_A(arow, q, g, C, cvec),
                            G::load_B(yn, q, g, C, HW, rowoff, w, W, row_ok, aligned4));
