@@ -49,6 +49,18 @@ template <> struct Elem<bf16_t> {
     __device__ __forceinline__ static float quant(float v) { return round_to_bf16(v); }
 };
 
+// Workgroup order across the chip.  Consecutive workgroup IDs are dispatched
+// round-robin over the 8 XCDs, each with its own L2; remapping so that every XCD
+// receives a contiguous run of logical tiles keeps tiles that share data (halo
+// rows, the channel blocks of one pixel tile) in the same L2.  Bijective for any
+// count.
+__device__ __forceinline__ int xcd_contiguous(int id, int count) {
+    constexpr int kXcd = 8;
+    const int q = count / kXcd, rem = count % kXcd;
+    const int xcd = id % kXcd, idx = id / kXcd;
+    return xcd * q + (xcd < rem ? xcd : rem) + idx;
+}
+
 // ---------------------------------------------------------------------------- MFMA
 // v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16] and B[l/16][l%16];
 // lane l receives D[4*(l/16) + v][l%16] in component v.

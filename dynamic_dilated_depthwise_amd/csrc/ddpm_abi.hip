@@ -29,9 +29,8 @@ int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype) {
     const double elems = (double)N * 3.0 * (double)C * K * K * (double)H * (double)W;
     if (elems > 4.0e18) return DDPM_ERR_INVALID_ARG;
     if ((double)N * H * W >= 2147483648.0) return DDPM_ERR_INVALID_ARG;
-    // Launch-grid limits of the spatial kernels (4-row tiles; N x channel blocks).
-    if ((H + 3) / 4 > kMaxGridYZ) return DDPM_ERR_UNSUPPORTED;
-    if (N * ((C + 15) / 16) > kMaxGridYZ) return DDPM_ERR_UNSUPPORTED;
+    // Launch-grid limit of the weight-gradient kernel (token splits x channel-block grid rows).
+    if (((C + 15) / 16) * ((C + 63) / 64) > kMaxGridYZ) return DDPM_ERR_UNSUPPORTED;
     return DDPM_OK;
 }
 
@@ -61,7 +60,6 @@ int ddpm_filter_fwd(const void *x, const void *taps, void *out, int64_t N, int64
     int st = check_shape(N, C, H, W, K, dtype);
     if (st != DDPM_OK) return st;
     if (bad_ptr(x, dtype) || bad_ptr(taps, dtype) || bad_ptr(out, dtype)) return DDPM_ERR_INVALID_ARG;
-    if (N * C > kMaxGridYZ) return DDPM_ERR_UNSUPPORTED;
     const int64_t es = dtype == DDPM_BF16 ? 2 : 4;
     const int64_t HW = H * W;
     const int64_t R = 3 * C * K * K;

@@ -37,10 +37,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nCB = (C + 15) >> 4;
-    const int n = blockIdx.z / nCB;
-    const int c0 = (blockIdx.z - n * nCB) * 16;
-    const int h = blockIdx.y * kRows + wave;
-    const int w = blockIdx.x * kCols + 4 * j;
+    // logical tile order: channel block fastest, then column tile, row band, image
+    const int ncolt = (W + kCols - 1) / kCols;
+    const int nbands = (H + kRows - 1) / kRows;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int c0 = (L % nCB) * 16;
+    L /= nCB;
+    const int w = (L % ncolt) * kCols + 4 * j;
+    L /= ncolt;
+    const int h = (L % nbands) * kRows + wave;
+    const int n = L / nbands;
     if (h >= H) return;  // no barriers in this kernel
     const int64_t HW = (int64_t)H * W;
     const bool aligned4 = al != 0;
@@ -165,10 +171,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nMG = (C + 63) >> 6;
-    const int n = blockIdx.z / nMG;
-    const int cm0 = (blockIdx.z - n * nMG) * 64;
-    const int h = blockIdx.y * kRows + wave;
-    const int w = blockIdx.x * kCols + 4 * j;
+    const int ncolt = (W + kCols - 1) / kCols;
+    const int nbands = (H + kRows - 1) / kRows;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int cm0 = (L % nMG) * 64;
+    L /= nMG;
+    const int w = (L % ncolt) * kCols + 4 * j;
+    L /= ncolt;
+    const int h = (L % nbands) * kRows + wave;
+    const int n = L / nbands;
     if (h >= H) return;
     const int64_t HW = (int64_t)H * W;
     const bool aligned4 = al != 0;
@@ -540,7 +551,9 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     const int iA = al ? 1 : 0;
     // dX
     if (gx != nullptr) {
-        dim3 grid((W + kCols - 1) / kCols, (H + kRows - 1) / kRows, N * ((C + 15) / 16));
+        const int64_t nblk = (int64_t)((W + kCols - 1) / kCols) * ((H + kRows - 1) / kRows) * N * ((C + 15) / 16);
+        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)nblk);
         const int nq = (C + Gen<T>::CH - 1) / Gen<T>::CH;
         auto args = [&](auto kern) {
             hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)y, (const T *)wg, (const T *)bg,
@@ -555,7 +568,9 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     }
     // dY
     if (gy != nullptr) {
-        dim3 grid((W + kCols - 1) / kCols, (H + kRows - 1) / kRows, N * ((C + 63) / 64));
+        const int64_t nblk = (int64_t)((W + kCols - 1) / kCols) * ((H + kRows - 1) / kRows) * N * ((C + 63) / 64);
+        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)nblk);
         const int mb = (C >= 64) ? 4 : (C + 15) / 16;
         auto args = [&](auto kern) {
             hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)x, (const T *)wg, (const T *)gout,

@@ -65,10 +65,16 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nCB = (C + 15) >> 4;
-    const int n = blockIdx.z / nCB;
-    const int c0 = (blockIdx.z - n * nCB) * 16;
-    const int h0 = blockIdx.y * kTileRows;
-    const int w0 = blockIdx.x * kTileCols;
+    // logical tile order: channel block fastest, then column tile, row band, image
+    const int ncolt = (W + kTileCols - 1) / kTileCols;
+    const int nbands = (H + kTileRows - 1) / kTileRows;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int c0 = (L % nCB) * 16;
+    L /= nCB;
+    const int w0 = (L % ncolt) * kTileCols;
+    L /= ncolt;
+    const int h0 = (L % nbands) * kTileRows;
+    const int n = L / nbands;
     const int64_t HW = (int64_t)H * W;
     const bool aligned4 = al != 0;
     const bool cvec = Elem<T>::is_bf16 ? (al != 0 && (C & 7) == 0) : (al != 0 && (C & 3) == 0);
@@ -181,8 +187,10 @@ static hipError_t launch_fused_t(const void *x, const void *y, const void *wg, c
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    dim3 grid((W + kTileCols - 1) / kTileCols, (H + kTileRows - 1) / kTileRows, N * ((C + 15) / 16));
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, (const T *)x, (const T *)y, (const T *)wg,
+    const int64_t nblk = (int64_t)((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows) * N *
+                         ((C + 15) / 16);
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), lds, stream, (const T *)x, (const T *)y, (const T *)wg,
                        (const T *)bg, (T *)out, C, H, W, al ? 1 : 0);
     return hipGetLastError();
 }
