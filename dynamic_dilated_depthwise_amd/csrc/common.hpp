@@ -118,6 +118,46 @@ __device__ __forceinline__ f32x4 load4_row(const T *__restrict__ row, int w, int
     return v;
 }
 
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+// Four consecutive pixels w..w+3 of a row with no bounds checks, for the case the
+// caller has shown (with wave-uniform tests) that every lane's run is in range:
+// w + 3 < W, and w >= 0 (w >= 1 when a bf16 run starts at an odd column).
+// `aligned4`: w % 4 == 0 and the row start is 16-byte (float) / 8-byte (bf16)
+// aligned; `row_even`: the row start is 4-byte aligned (bf16 only); `odd`: w is
+// odd (bf16 only; a wave-uniform property of the shift).
+template <typename T>
+__device__ __forceinline__ f32x4 load4_unchecked(const T *__restrict__ row, int w, bool aligned4, bool row_even,
+                                                 bool odd) {
+    f32x4 v;
+    if constexpr (Elem<T>::is_bf16) {
+        if (aligned4) {
+            const u16x4 u = *(const u16x4 *)(row + w);
+            v[0] = bf16_bits_to_f32(u[0]); v[1] = bf16_bits_to_f32(u[1]);
+            v[2] = bf16_bits_to_f32(u[2]); v[3] = bf16_bits_to_f32(u[3]);
+        } else if (row_even && !odd) {
+            const u32x2_a4 d = *(const u32x2_a4 *)(row + w);
+            v[0] = __uint_as_float(d[0] << 16); v[1] = __uint_as_float(d[0] & 0xffff0000u);
+            v[2] = __uint_as_float(d[1] << 16); v[3] = __uint_as_float(d[1] & 0xffff0000u);
+        } else if (row_even) {
+            const u32x2_a4 d = *(const u32x2_a4 *)(row + w - 1);
+            v[0] = __uint_as_float(d[0] & 0xffff0000u); v[1] = __uint_as_float(d[1] << 16);
+            v[2] = __uint_as_float(d[1] & 0xffff0000u); v[3] = bf16_bits_to_f32(row[w + 3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = bf16_bits_to_f32(row[w + k]);
+        }
+    } else {
+        if (aligned4) {
+            v = *(const f32x4 *)(row + w);
+        } else {
+            const f32x4_a4 t = *(const f32x4_a4 *)(row + w);
+            v = t;
+        }
+    }
+    return v;
+}
+
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint16_t u16x8_a16 __attribute__((ext_vector_type(8), aligned(16)));
 
@@ -161,6 +201,36 @@ __device__ __forceinline__ void load8_bf16_row(const bf16_t *__restrict__ row, i
     }
 }
 
+// Eight bf16 pixels w..w+7 with no bounds checks (caller: w + 7 < W, and w >= 1 when
+// w is odd).  `al16`: w % 8 == 0 with 16-byte aligned rows; `row_even`: 4-byte
+// aligned rows; `odd`: w is odd (wave-uniform).
+__device__ __forceinline__ void load8_bf16_unchecked(const bf16_t *__restrict__ row, int w, bool al16, bool row_even,
+                                                     bool odd, float (&v)[8]) {
+    if (al16) {
+        const u16x8 u = *(const u16x8_a16 *)(row + w);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = bf16_bits_to_f32(u[k]);
+    } else if (row_even && !odd) {
+        const u32x4_a4 d = *(const u32x4_a4 *)(row + w);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(d[k] << 16);
+            v[2 * k + 1] = __uint_as_float(d[k] & 0xffff0000u);
+        }
+    } else if (row_even) {
+        const u32x4_a4 d = *(const u32x4_a4 *)(row + w - 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(d[k] & 0xffff0000u);
+            if (k < 3) v[2 * k + 1] = __uint_as_float(d[k + 1] << 16);
+        }
+        v[7] = bf16_bits_to_f32(row[w + 7]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = bf16_bits_to_f32(row[w + k]);
+    }
+}
+
 // RL consecutive pixels of a row as float: 4 for float32 tensors, 8 for bf16.
 template <typename T, int RL> struct RowRun;
 template <> struct RowRun<float, 4> {
@@ -169,11 +239,21 @@ template <> struct RowRun<float, 4> {
         const f32x4 t = load4_row(row, w, W, ok, al && ((w & 3) == 0));
         v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
     }
+    // No bounds checks; `wal`: the run is vector-aligned (w % 4 == 0, aligned rows).
+    __device__ __forceinline__ static void load_fast(const float *__restrict__ row, int w, bool wal, bool, bool,
+                                                     float (&v)[4]) {
+        const f32x4 t = load4_unchecked(row, w, wal, true, false);
+        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    }
 };
 template <> struct RowRun<bf16_t, 8> {
     __device__ __forceinline__ static void load(const bf16_t *__restrict__ row, int w, int W, bool ok, bool,
                                                 float (&v)[8]) {
         load8_bf16_row(row, w, W, ok, v);
+    }
+    __device__ __forceinline__ static void load_fast(const bf16_t *__restrict__ row, int w, bool wal, bool row_even,
+                                                     bool odd, float (&v)[8]) {
+        load8_bf16_unchecked(row, w, wal, row_even, odd, v);
     }
 };
 

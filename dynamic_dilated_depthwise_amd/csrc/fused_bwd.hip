@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     constexpr int r = (K - 1) / 2;
     constexpr int KK = K * K;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nCB = (C + 15) >> 4;
@@ -55,6 +55,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     const T *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
     const int nq = KQ > 0 ? KQ : (C + G::CH - 1) / G::CH;
     const int cA = c0 + j;
+    const int w0 = w - 4 * j;  // tile's first column (wave-uniform)
+    // Wave-uniform: all 16 channels exist, every weight chunk is whole and vector-aligned.
+    // (KQ chunks must cover exactly C channels: the fp32 KQ=4 instance also serves C = 48;
+    // the streamed KQ=0 instance only visits chunks q < nq.)
+    const bool full = (c0 + 16 <= C) && cvec && (C % G::CH == 0) && (KQ == 0 || KQ * G::CH == C);
 
     float dacc[4][4];
 #pragma unroll
@@ -80,9 +85,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
             const int dc = (kj - r) * D;
             const bool rs_ok = hs >= 0 && hs < H;
             const int64_t rowoff = (int64_t)(rs_ok ? hs : 0) * W;
-            const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
-            st.a = G::load_A(arow, q, g, C, cvec);
-            st.y = G::load_B(yn, q, g, C, HW, rowoff, w - dc, W, rs_ok, aligned4 && ((dc & 3) == 0));
+            // wave-uniform: the shifted row exists and all 64 shifted columns are inside it
+            const int odd = dc & 1;
+            if (full && rs_ok && w0 - dc - odd >= 0 && w0 + kCols - 1 - dc < W) {
+                st.a = G::load_A_fast(wg + ((int64_t)(b * C + cA) * KK + t) * C, q, g);
+                st.y = G::load_B_fast(yn, q, g, HW, rowoff, w - dc, aligned4 && ((dc & 3) == 0), aligned4, odd);
+            } else {
+                const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
+                st.a = G::load_A(arow, q, g, C, cvec);
+                st.y = G::load_B(yn, q, g, C, HW, rowoff, w - dc, W, rs_ok, aligned4 && ((dc & 3) == 0));
+            }
         };
         Step cur;
         fetch(0, 0, cur);
@@ -103,11 +115,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
             }
             // G_b at the source pixels (consumed after the MFMAs)
             f32x4 gs[4];
+            const int dcs = (kj - r) * D;
+            const int odd = dcs & 1;
+            if (full && rs_ok && w0 - dcs - odd >= 0 && w0 + kCols - 1 - dcs < W) {  // wave-uniform
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int c = c0 + 4 * g + v;
-                gs[v] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, ws, W, rs_ok && c < C,
-                                  al_s);
+                for (int v = 0; v < 4; ++v)
+                    gs[v] = load4_unchecked(gn + (int64_t)((1 + b) * C + c0 + 4 * g + v) * HW + rowoff, ws, al_s,
+                                            aligned4, odd);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int c = c0 + 4 * g + v;
+                    gs[v] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, ws, W,
+                                      rs_ok && c < C, al_s);
+                }
             }
             f32x4 acc[4];
 #pragma unroll
@@ -152,12 +173,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
 
 // ============================================================================ dY
 // dY = W^T dK as an MFMA product: rows = output channels c' (16 per block, MB
-// blocks per wave), columns = the wave's 64 pixels (4 per lane), contraction over
-// the generator rows o = (b, c, t).  The B operand dK[o, p] = G_b[c, p] *
+// blocks), columns = one 64-pixel row segment (4 pixels per lane), contraction
+// over the generator rows o = (b, c, t).  The B operand dK[o, p] = G_b[c, p] *
 // x[c, p + d_bt] is formed in registers from G and the shifted x and never stored.
 //   float32: one k-step = 4 generator rows (b, 4cq + g, t), lane group g;
 //   bfloat16: one k-step = 32 generator rows (b, 32cq + 8g + e, t); dK is rounded
 //   to bfloat16 as the MFMA operand.
+// The contraction items (channel chunk cq, branch b, tap t) are split into four
+// contiguous ranges, one per wave, and the four partial products are summed in a
+// fixed order through LDS, so one workgroup per row segment still fills the chip.
 template <typename T, int K, int MB>
 __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x, const T *__restrict__ wg,
                                                         const T *__restrict__ gout, T *__restrict__ gy, int C, int H,
@@ -166,21 +190,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
     constexpr int KK = K * K;
     constexpr bool BF = Elem<T>::is_bf16;
     constexpr int CK = BF ? 32 : 4;  // generator channels per k-step
+    __shared__ f32x4 red[3][MB * 4][64];
+
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nMG = (C + 63) >> 6;
     const int ncolt = (W + kCols - 1) / kCols;
-    const int nbands = (H + kRows - 1) / kRows;
     int L = xcd_contiguous(blockIdx.x, gridDim.x);
     const int cm0 = (L % nMG) * 64;
     L /= nMG;
     const int w = (L % ncolt) * kCols + 4 * j;
     L /= ncolt;
-    const int h = (L % nbands) * kRows + wave;
-    const int n = L / nbands;
-    if (h >= H) return;
+    const int h = L % H;
+    const int n = L / H;
     const int64_t HW = (int64_t)H * W;
     const bool aligned4 = al != 0;
     const T *__restrict__ xn = x + (int64_t)n * C * HW;
@@ -193,94 +217,148 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[m][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    const int w0 = w - 4 * j;  // row segment's first column (wave-uniform)
+    // Wave-uniform: every generator channel chunk, output channel and column exists.
+    const bool full = (C % CK == 0) && (cm0 + 16 * MB <= C) && (w0 + kCols <= W);
     const int ncq = (C + CK - 1) / CK;
-#pragma unroll 1
-    for (int cq = 0; cq < ncq; ++cq) {
-#pragma unroll
-        for (int b = 0; b < 3; ++b) {
+    const int nitems = ncq * 3 * KK;  // (cq, b, t), t fastest
+    const int i0 = (int)((int64_t)nitems * wave / 4);
+    const int i1 = (int)((int64_t)nitems * (wave + 1) / 4);
+
+    if constexpr (!BF) {
+        // Operands of one item, fetched one item ahead of its MFMAs.
+        struct Ops {
+            f32x4 gb, xs;
+            float a[MB];
+        };
+        auto fetch = [&](int i, Ops &o) {
+            const int t = i % KK;
+            const int pr = i / KK;
+            const int b = pr % 3;
+            const int c = CK * (pr / 3) + g;
+            const bool c_ok = c < C;
             const int D = dilation(b);
-            if constexpr (!BF) {
-                const int c = CK * cq + g;
-                const bool c_ok = c < C;
-                const f32x4 gb = load4_row(gn + (int64_t)((1 + b) * C + (c_ok ? c : 0)) * HW + rowoff, w, W, c_ok,
-                                           aligned4);
-                // x at the tap's shifted pixels and the weight column fragments of
-                // tap t, fetched one tap ahead of their MFMAs.
-                auto fetch = [&](int t, f32x4 &xs, float (&a)[MB]) {
-                    const int ki = t / K;
-                    const int kj = t - ki * K;
-                    const int hh = h + (ki - r) * D;
-                    const int dc = (kj - r) * D;
-                    const bool rok = c_ok && hh >= 0 && hh < H;
-                    xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(rok ? hh : 0) * W, w + dc, W, rok,
-                                   aligned4 && ((dc & 3) == 0));
-                    const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+            const int ki = t / K;
+            const int kj = t - ki * K;
+            const int hh = h + (ki - r) * D;
+            const int dc = (kj - r) * D;
+            if (full && hh >= 0 && hh < H && w0 + dc - (dc & 1) >= 0 && w0 + kCols - 1 + dc < W) {  // wave-uniform
+                o.gb = load4_unchecked(gn + (int64_t)((1 + b) * C + c) * HW + rowoff, w, aligned4, true, false);
+                o.xs = load4_unchecked(xn + (int64_t)c * HW + (int64_t)hh * W, w + dc, aligned4 && ((dc & 3) == 0),
+                                       true, false);
+                const T *wrow = wg + ((int64_t)(b * C + c) * KK + t) * C + cm0 + j;
 #pragma unroll
-                    for (int m = 0; m < MB; ++m) {
-                        const int cp = cm0 + 16 * m + j;
-                        a[m] = (c_ok && cp < C) ? wrow[cp] : 0.f;
-                    }
-                };
-                f32x4 xn_;
-                float an_[MB];
-                fetch(0, xn_, an_);
+                for (int m = 0; m < MB; ++m) o.a[m] = wrow[16 * m];
+                return;
+            }
+            const bool rok = c_ok && hh >= 0 && hh < H;
+            o.gb = load4_row(gn + (int64_t)((1 + b) * C + (c_ok ? c : 0)) * HW + rowoff, w, W, c_ok, aligned4);
+            o.xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(rok ? hh : 0) * W, w + dc, W, rok,
+                             aligned4 && ((dc & 3) == 0));
+            const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const int cp = cm0 + 16 * m + j;
+                o.a[m] = (c_ok && cp < C) ? wrow[cp] : 0.f;
+            }
+        };
+        Ops nxt;
+        if (i0 < i1) fetch(i0, nxt);
 #pragma unroll 1
-                for (int t = 0; t < KK; ++t) {
-                    const f32x4 xs = xn_;
-                    float a[MB];
+        for (int i = i0; i < i1; ++i) {
+            const Ops cur = nxt;
+            if (i + 1 < i1) fetch(i + 1, nxt);
 #pragma unroll
-                    for (int m = 0; m < MB; ++m) a[m] = an_[m];
-                    if (t + 1 < KK) fetch(t + 1, xn_, an_);
+            for (int m = 0; m < MB; ++m)
 #pragma unroll
-                    for (int m = 0; m < MB; ++m)
-#pragma unroll
-                        for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x4_f32(a[m], gb[pb] * xs[pb], acc[m][pb]);
-                }
-            } else {
-                f32x4 gb[8];
+                for (int pb = 0; pb < 4; ++pb)
+                    acc[m][pb] = mfma_16x16x4_f32(cur.a[m], cur.gb[pb] * cur.xs[pb], acc[m][pb]);
+        }
+    } else {
+        f32x4 gb[8];
+        int cur_pair = -1;
+#pragma unroll 1
+        for (int i = i0; i < i1; ++i) {
+            const int t = i % KK;
+            const int pr = i / KK;
+            const int b = pr % 3;
+            const int cq = pr / 3;
+            const int D = dilation(b);
+            if (pr != cur_pair) {  // wave-uniform: a new (channel chunk, branch) pair
+                cur_pair = pr;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int c = CK * cq + 8 * g + e;
-                    gb[e] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, w, W, c < C,
-                                      aligned4);
+                    if (full)
+                        gb[e] = load4_unchecked(gn + (int64_t)((1 + b) * C + c) * HW + rowoff, w, aligned4, aligned4,
+                                                false);
+                    else
+                        gb[e] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, w, W, c < C,
+                                          aligned4);
                 }
-#pragma unroll 1
-                for (int t = 0; t < KK; ++t) {
-                    const int ki = t / K;
-                    const int kj = t - ki * K;
-                    const int hh = h + (ki - r) * D;
-                    const int dc = (kj - r) * D;
-                    const bool hok = hh >= 0 && hh < H;
-                    uint16_t bv[4][8];
-                    uint16_t av[MB][8];
+            }
+            const int ki = t / K;
+            const int kj = t - ki * K;
+            const int hh = h + (ki - r) * D;
+            const int dc = (kj - r) * D;
+            const bool hok = hh >= 0 && hh < H;
+            uint16_t bv[4][8];
+            uint16_t av[MB][8];
+            if (full && hok && w0 + dc - (dc & 1) >= 0 && w0 + kCols - 1 + dc < W) {  // wave-uniform
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int c = CK * cq + 8 * g + e;
-                        const bool c_ok = c < C;
-                        const f32x4 xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(hok ? hh : 0) * W,
-                                                   w + dc, W, c_ok && hok, aligned4 && ((dc & 3) == 0));
+                for (int e = 0; e < 8; ++e) {
+                    const int c = CK * cq + 8 * g + e;
+                    const f32x4 xs = load4_unchecked(xn + (int64_t)c * HW + (int64_t)hh * W, w + dc,
+                                                     aligned4 && ((dc & 3) == 0), aligned4, (dc & 1) != 0);
 #pragma unroll
-                        for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
-                        const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+                    for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
+                    const T *wrow = wg + ((int64_t)(b * C + c) * KK + t) * C + cm0 + j;
 #pragma unroll
-                        for (int m = 0; m < MB; ++m) {
-                            const int cp = cm0 + 16 * m + j;
-                            av[m][e] = (c_ok && cp < C) ? wrow[cp] : (uint16_t)0;
-                        }
-                    }
-                    bf16x8 bq[4];
-#pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) bq[pb] = pack_bf16x8(bv[pb]);
-#pragma unroll
-                    for (int m = 0; m < MB; ++m) {
-                        const bf16x8 aq = pack_bf16x8(av[m]);
-#pragma unroll
-                        for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x32_bf16(aq, bq[pb], acc[m][pb]);
-                    }
+                    for (int m = 0; m < MB; ++m) av[m][e] = wrow[16 * m];
                 }
+            } else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = CK * cq + 8 * g + e;
+                const bool c_ok = c < C;
+                const f32x4 xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(hok ? hh : 0) * W, w + dc, W,
+                                           c_ok && hok, aligned4 && ((dc & 3) == 0));
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
+                const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const int cp = cm0 + 16 * m + j;
+                    av[m][e] = (c_ok && cp < C) ? wrow[cp] : (uint16_t)0;
+                }
+            }
+            bf16x8 bq[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) bq[pb] = pack_bf16x8(bv[pb]);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const bf16x8 aq = pack_bf16x8(av[m]);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x32_bf16(aq, bq[pb], acc[m][pb]);
             }
         }
     }
+
+    // Fixed-order sum of the four waves' partial products: ((w0 + w1) + w2) + w3.
+    if (wave > 0) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) red[wave - 1][m * 4 + pb][lane] = acc[m][pb];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll 1
+    for (int k = 0; k < 3; ++k)  // one wave's slice at a time keeps the register peak low
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc[m][pb] += red[k][m * 4 + pb][lane];
 
     T *__restrict__ yo = gy + (int64_t)n * C * HW;
 #pragma unroll
@@ -318,7 +396,7 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
     __shared__ float redb[4][4][16];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int g = lane >> 4;
     const int j = lane & 15;
     const int combo0 = blockIdx.x * CG;
@@ -379,59 +457,102 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
     }
     const bool al = ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)gout % 16 == 0) &&
                     (W % 4 == 0);
-    while (p0 < t1) {
-        float a[CG][RL];
-        float bvals[NB][RL];
+    const bool chfull = c0 + 16 <= C;            // all 16 depthwise channels exist (wave-uniform)
+    const bool cpfull = cn0 + 16 * NB <= C;      // all NB blocks of c' exist (wave-uniform)
+    // Raw operands of one chunk: G_b and shifted x per (b, t) pair (their product is
+    // the A operand dK), y per c' block (the B operand).
+    struct Raw {
+        float gv[CG][RL];
+        float xv[CG][RL];
+        float yv[NB][RL];
+    };
+    // For loading, a (b, t) slot past the last pair reads the b = 0, zero-shift
+    // plane (always valid); its product is zeroed by cb_valid at consumption.
+    int cb_bl[CG];
+    float cb_valid[CG];
+#pragma unroll
+    for (int cc = 0; cc < CG; ++cc) {
+        cb_bl[cc] = cb_b[cc] >= 0 ? cb_b[cc] : 0;
+        cb_valid[cc] = cb_b[cc] >= 0 ? 1.f : 0.f;
+    }
+    auto load_chunk = [&](int64_t q0, int qn, int qh, int qw, Raw &o) {
+        const bool in_row = (q0 + KC <= t1) && (qw + KC <= W);
+        // Wave-uniform: the whole chunk is one row segment, every channel exists and
+        // every shifted run lies inside its row -> one straight-line block of loads.
+        bool fast = in_row && chfull && cpfull;
+#pragma unroll
+        for (int cc = 0; cc < CG; ++cc) {
+            const int hs = qh + cb_dr[cc];
+            const int dc = cb_dc[cc];
+            fast = fast && hs >= 0 && hs < H && qw + dc - ((qw + dc) & 1) >= 0 && qw + KC - 1 + dc < W;
+        }
+        if (fast) {
+            const int w = qw + RL * g;
+            const T *xn = x + (int64_t)qn * CHW;
+            const T *gn = gout + (int64_t)qn * 4 * CHW;
+            const T *yn = y + (int64_t)qn * CHW;
+            const int64_t rowoff = (int64_t)qh * W;
+            const bool wal = al && (qw % RL == 0) && (!BF || (W % 8 == 0));  // unshifted runs vector-aligned
+            const bool odd = (qw & 1) != 0;
+#pragma unroll
+            for (int cc = 0; cc < CG; ++cc) {
+                const int dc = cb_dc[cc];
+                RowRun<T, RL>::load_fast(gn + (int64_t)((1 + cb_bl[cc]) * C + cA) * HW + rowoff, w, wal, al, odd,
+                                         o.gv[cc]);
+                RowRun<T, RL>::load_fast(xn + (int64_t)cA * HW + (int64_t)(qh + cb_dr[cc]) * W, w + dc,
+                                         wal && (dc % RL == 0), al, ((qw + dc) & 1) != 0, o.xv[cc]);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                RowRun<T, RL>::load_fast(yn + (int64_t)(cn0 + 16 * nb + j) * HW + rowoff, w, wal, al, odd, o.yv[nb]);
+            return;
+        }
 #pragma unroll
         for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
-            for (int k = 0; k < RL; ++k) a[cc][k] = 0.f;
+            for (int k = 0; k < RL; ++k) o.gv[cc][k] = o.xv[cc][k] = 0.f;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int k = 0; k < RL; ++k) bvals[nb][k] = 0.f;
-
-        if (p0 + KC <= t1 && pw + KC <= W) {
-            const int w = pw + RL * g;
-            const T *xn = x + (int64_t)pn * CHW;
-            const T *gn = gout + (int64_t)pn * 4 * CHW;
-            const T *yn = y + (int64_t)pn * CHW;
-            const int64_t rowoff = (int64_t)ph * W;
+            for (int k = 0; k < RL; ++k) o.yv[nb][k] = 0.f;
+        if (in_row) {
+            const int w = qw + RL * g;
+            const T *xn = x + (int64_t)qn * CHW;
+            const T *gn = gout + (int64_t)qn * 4 * CHW;
+            const T *yn = y + (int64_t)qn * CHW;
+            const int64_t rowoff = (int64_t)qh * W;
 #pragma unroll
             for (int cc = 0; cc < CG; ++cc) {
                 const int b = cb_b[cc];
                 if (b >= 0 && cA_ok) {
-                    float gv[RL], xv[RL];
-                    RowRun<T, RL>::load(gn + (int64_t)((1 + b) * C + cA) * HW + rowoff, w, W, true, al, gv);
-                    const int hs = ph + cb_dr[cc];
+                    RowRun<T, RL>::load(gn + (int64_t)((1 + b) * C + cA) * HW + rowoff, w, W, true, al, o.gv[cc]);
+                    const int hs = qh + cb_dr[cc];
                     const bool hok = hs >= 0 && hs < H;
                     RowRun<T, RL>::load(xn + (int64_t)cA * HW + (int64_t)(hok ? hs : 0) * W, w + cb_dc[cc], W, hok,
-                                        al, xv);
-#pragma unroll
-                    for (int k = 0; k < RL; ++k) a[cc][k] = gv[k] * xv[k];
+                                        al, o.xv[cc]);
                 }
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int cp = cn0 + 16 * nb + j;
-                if (cp < C) RowRun<T, RL>::load(yn + (int64_t)cp * HW + rowoff, w, W, true, al, bvals[nb]);
+                if (cp < C) RowRun<T, RL>::load(yn + (int64_t)cp * HW + rowoff, w, W, true, al, o.yv[nb]);
             }
         } else {
-            const int64_t pf = p0 + (int64_t)g * RL;  // this lane's first token
-            int n = pn, hh = ph, ww = pw + RL * g;
+            const int64_t pf = q0 + (int64_t)g * RL;  // this lane's first token
+            int nn = qn, hh = qh, ww = qw + RL * g;
             while (ww >= W) {
                 ww -= W;
                 if (++hh == H) {
                     hh = 0;
-                    ++n;
+                    ++nn;
                 }
             }
 #pragma unroll
             for (int k = 0; k < RL; ++k) {
                 if (pf + k < t1) {
-                    const T *xn = x + (int64_t)n * CHW;
-                    const T *gn = gout + (int64_t)n * 4 * CHW;
-                    const T *yn = y + (int64_t)n * CHW;
+                    const T *xn = x + (int64_t)nn * CHW;
+                    const T *gn = gout + (int64_t)nn * 4 * CHW;
+                    const T *yn = y + (int64_t)nn * CHW;
                     const int64_t pix = (int64_t)hh * W + ww;
 #pragma unroll
                     for (int cc = 0; cc < CG; ++cc) {
@@ -440,31 +561,47 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
                             const int hs = hh + cb_dr[cc];
                             const int ws = ww + cb_dc[cc];
                             if (hs >= 0 && hs < H && ws >= 0 && ws < W) {
-                                const float gv = Elem<T>::to_f32(gn[(int64_t)((1 + b) * C + cA) * HW + pix]);
-                                const float xv = Elem<T>::to_f32(xn[(int64_t)cA * HW + (int64_t)hs * W + ws]);
-                                a[cc][k] = gv * xv;
+                                o.gv[cc][k] = Elem<T>::to_f32(gn[(int64_t)((1 + b) * C + cA) * HW + pix]);
+                                o.xv[cc][k] = Elem<T>::to_f32(xn[(int64_t)cA * HW + (int64_t)hs * W + ws]);
                             }
                         }
                     }
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         const int cp = cn0 + 16 * nb + j;
-                        if (cp < C) bvals[nb][k] = Elem<T>::to_f32(yn[(int64_t)cp * HW + pix]);
+                        if (cp < C) o.yv[nb][k] = Elem<T>::to_f32(yn[(int64_t)cp * HW + pix]);
                     }
                 }
                 if (++ww == W) {
                     ww = 0;
                     if (++hh == H) {
                         hh = 0;
-                        ++n;
+                        ++nn;
                     }
                 }
             }
         }
+    };
+    auto advance = [&](int64_t &q0, int &qn, int &qh, int &qw) {
+        q0 += 4 * KC;
+        qw += 4 * KC;
+        while (qw >= W) {
+            qw -= W;
+            if (++qh == H) {
+                qh = 0;
+                ++qn;
+            }
+        }
+    };
+    auto consume = [&](const Raw &o) {
+        float a[CG][RL];
 #pragma unroll
         for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
-            for (int k = 0; k < RL; ++k) dbacc[cc] += a[cc][k];
+            for (int k = 0; k < RL; ++k) {
+                a[cc][k] = o.gv[cc][k] * o.xv[cc][k] * cb_valid[cc];
+                dbacc[cc] += a[cc][k];
+            }
         if constexpr (!BF) {
 #pragma unroll
             for (int k = 0; k < RL; ++k)
@@ -472,14 +609,14 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
                 for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
-                        acc[cc][nb] = mfma_16x16x4_f32(a[cc][k], bvals[nb][k], acc[cc][nb]);
+                        acc[cc][nb] = mfma_16x16x4_f32(a[cc][k], o.yv[nb][k], acc[cc][nb]);
         } else {
             bf16x8 bq[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 uint16_t u[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) u[k] = f32_to_bf16_bits(bvals[nb][k]);  // exact: y is bf16
+                for (int k = 0; k < 8; ++k) u[k] = f32_to_bf16_bits(o.yv[nb][k]);  // exact: y is bf16
                 bq[nb] = pack_bf16x8(u);
             }
 #pragma unroll
@@ -492,15 +629,24 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
                 for (int nb = 0; nb < NB; ++nb) acc[cc][nb] = mfma_16x16x32_bf16(aq, bq[nb], acc[cc][nb]);
             }
         }
-        // advance to this wave's next chunk
-        p0 += 4 * KC;
-        pw += 4 * KC;
-        while (pw >= W) {
-            pw -= W;
-            if (++ph == H) {
-                ph = 0;
-                ++pn;
-            }
+    };
+
+    if constexpr (!BF) {
+        // float32: the next chunk's loads are issued before this chunk's MFMAs.
+        Raw nxt;
+        if (p0 < t1) load_chunk(p0, pn, ph, pw, nxt);
+        while (p0 < t1) {
+            const Raw cur = nxt;
+            advance(p0, pn, ph, pw);
+            if (p0 < t1) load_chunk(p0, pn, ph, pw, nxt);
+            consume(cur);
+        }
+    } else {
+        while (p0 < t1) {
+            Raw cur;
+            load_chunk(p0, pn, ph, pw, cur);
+            consume(cur);
+            advance(p0, pn, ph, pw);
         }
     }
 
@@ -561,14 +707,16 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
         };
         if (nq == 1) args(bwd_dx_kernel<T, K, 1>);
         else if (nq == 2) args(bwd_dx_kernel<T, K, 2>);
-        else if (!Elem<T>::is_bf16 && nq <= 4) args(bwd_dx_kernel<T, K, 4>);
-        else args(bwd_dx_kernel<T, K, 0>);
+        else if constexpr (!Elem<T>::is_bf16) {
+            if (nq <= 4) args(bwd_dx_kernel<T, K, 4>);
+            else args(bwd_dx_kernel<T, K, 0>);
+        } else args(bwd_dx_kernel<T, K, 0>);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // dY
     if (gy != nullptr) {
-        const int64_t nblk = (int64_t)((W + kCols - 1) / kCols) * ((H + kRows - 1) / kRows) * N * ((C + 63) / 64);
+        const int64_t nblk = (int64_t)((W + kCols - 1) / kCols) * H * N * ((C + 63) / 64);
         if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         const dim3 grid((unsigned)nblk);
         const int mb = (C >= 64) ? 4 : (C + 15) / 16;
@@ -584,7 +732,9 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     }
     // dW / db partials
     if (dwp != nullptr) {
-        constexpr int CG = 4;
+        // (b, t) pairs per workgroup: bf16 token runs are twice as long, so fewer
+        // pairs keep the prefetched operands inside the register budget.
+        constexpr int CG = Elem<T>::is_bf16 ? 2 : 4;
         constexpr int NCOMBO = 3 * K * K;
         dim3 grid((NCOMBO + CG - 1) / CG, ((C + 15) / 16) * ((C + 63) / 64), S);
         const int nb = (C >= 64) ? 4 : (C + 15) / 16;

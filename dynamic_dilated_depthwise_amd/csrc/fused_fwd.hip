@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     extern __shared__ float xs[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nCB = (C + 15) >> 4;
@@ -97,6 +97,9 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     __syncthreads();
 
     const int cA = c0 + j;  // channel of the generator row this lane supplies
+    // Wave-uniform: all 16 channels exist, every weight chunk is whole and vector-aligned.
+    // (KQ chunks must cover exactly C channels: the fp32 KQ=4 instance also serves C = 48.)
+    const bool full = (c0 + 16 <= C) && cvec && (KQ * G::CH == C);
     float oacc[3][4][4];    // [branch][v][pb]
 #pragma unroll
     for (int b = 0; b < 3; ++b)
@@ -110,6 +113,15 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
         const int D = dilation(b);
         // Generator-row operand and bias of tap t of this branch.
         auto fetch = [&](int t, typename G::AFrag (&af)[KQ > 0 ? KQ : 1], float (&bf)[4]) {
+            if (full) {  // wave-uniform: every row and column exists
+                const T *arow = wg + ((int64_t)(b * C + cA) * KK + t) * C;
+#pragma unroll
+                for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) af[q] = G::load_A_fast(arow, q, g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    bf[v] = Elem<T>::to_f32(bg[(int64_t)(b * C + c0 + 4 * g + v) * KK + t]);
+                return;
+            }
             const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
 #pragma unroll
             for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) af[q] = G::load_A(arow, q, g, C, cvec);

@@ -41,6 +41,22 @@ template <> struct Gen<float> {
         }
         return b;
     }
+    // As load_B with every lane's run known to be in range (wave-uniform test by the
+    // caller): no per-lane bounds checks.  `w_al`: w % 4 == 0 with aligned rows.
+    __device__ __forceinline__ static BFrag load_B_fast(const float *__restrict__ yn, int q, int g, int64_t HW,
+                                                        int64_t rowoff, int w, bool w_al, bool, bool) {
+        BFrag b;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            b.v[s] = load4_unchecked(yn + (int64_t)(16 * q + 4 * g + s) * HW + rowoff, w, w_al, true, false);
+        return b;
+    }
+    // As load_A for an existing row with C % 4 == 0 and a 16-byte aligned weight.
+    __device__ __forceinline__ static AFrag load_A_fast(const float *__restrict__ arow, int q, int g) {
+        AFrag a;
+        a.v = *(const f32x4 *)(arow + 16 * q + 4 * g);
+        return a;
+    }
     // Weight row `arow` (nullptr when the row does not exist), columns 16q+4g..+3.
     __device__ __forceinline__ static AFrag load_A(const float *__restrict__ arow, int q, int g, int C, bool c4) {
         AFrag a;
@@ -101,6 +117,47 @@ template <> struct Gen<bf16_t> {
             b.v[pb] = pack_bf16x8(col);
         }
         return b;
+    }
+    // Four raw bf16 values at row[w..w+3] with no bounds checks (see load4_unchecked).
+    __device__ __forceinline__ static void load4_raw_fast(const bf16_t *__restrict__ row, int w, bool w_al,
+                                                          bool row_even, bool odd, uint16_t (&o)[4]) {
+        if (w_al) {
+            const u16x4 u = *(const u16x4 *)(row + w);
+            o[0] = u[0]; o[1] = u[1]; o[2] = u[2]; o[3] = u[3];
+        } else if (row_even && !odd) {
+            const u32x2_a4 d = *(const u32x2_a4 *)(row + w);
+            o[0] = (uint16_t)d[0]; o[1] = (uint16_t)(d[0] >> 16);
+            o[2] = (uint16_t)d[1]; o[3] = (uint16_t)(d[1] >> 16);
+        } else if (row_even) {
+            const u32x2_a4 d = *(const u32x2_a4 *)(row + w - 1);
+            o[0] = (uint16_t)(d[0] >> 16); o[1] = (uint16_t)d[1];
+            o[2] = (uint16_t)(d[1] >> 16); o[3] = row[w + 3];
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = row[w + k];
+        }
+    }
+    __device__ __forceinline__ static BFrag load_B_fast(const bf16_t *__restrict__ yn, int q, int g, int64_t HW,
+                                                        int64_t rowoff, int w, bool w_al, bool row_even, bool odd) {
+        uint16_t v[8][4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            load4_raw_fast(yn + (int64_t)(32 * q + 8 * g + e) * HW + rowoff, w, w_al, row_even, odd, v[e]);
+        BFrag b;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            uint16_t col[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) col[e] = v[e][pb];
+            b.v[pb] = pack_bf16x8(col);
+        }
+        return b;
+    }
+    // As load_A for an existing row with C % 8 == 0 and a 16-byte aligned weight.
+    __device__ __forceinline__ static AFrag load_A_fast(const bf16_t *__restrict__ arow, int q, int g) {
+        AFrag a;
+        a.v = __builtin_bit_cast(bf16x8, *(const u16x8 *)(arow + 32 * q + 8 * g));
+        return a;
     }
     __device__ __forceinline__ static AFrag load_A(const bf16_t *__restrict__ arow, int q, int g, int C, bool c8) {
         const int c = 32 * q + 8 * g;
