@@ -68,6 +68,47 @@ def algorithmic(shape, dtype_bytes, S):
 KERNEL_BOUND = {"filter": "hbm", "fused_fwd": "mfma", "bwd_dx": "mfma", "bwd_dy": "mfma", "bwd_dw": "mfma",
                 "reduce": "hbm"}
 
+# Kernel symbol and the source files that define it (for the traffic record's digest).
+KERNEL_SYMBOL = {"filter": "filter_fwd_kernel", "fused_fwd": "fused_fwd_kernel", "bwd_dx": "bwd_dx_kernel",
+                 "bwd_dy": "bwd_dy_kernel", "bwd_dw": "bwd_dw_kernel", "reduce": "reduce_partials_kernel"}
+KERNEL_SOURCES = {
+    "filter": ["filter_fwd.hip", "common.hpp"],
+    "fused_fwd": ["fused_fwd.hip", "gen_mma.hpp", "common.hpp"],
+    "bwd_dx": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
+    "bwd_dy": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
+    "bwd_dw": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
+    "reduce": ["reduce.hip", "common.hpp"],
+}
+CSRC = os.path.join(ROOT, "dynamic_dilated_depthwise_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest(name):
+    """sha256 over the source files of one kernel, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name, workload, dtype):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 counter record
+    (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or None when there
+    is no record or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{workload}_{dtype}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 4 and parts[0] == "traffic:" and parts[1] == KERNEL_SYMBOL[name]:
+            fields = dict(p.split("=", 1) for p in parts[2:] if "=" in p)
+            if fields.get("source") == kernel_source_digest(name):
+                return int(fields["bytes"])
+            return None
+    return None
+
 
 def run_cpu_baseline(h, shape):
     """The fp64 oracle on the same inputs: one full step, timed on the host cores."""
@@ -205,12 +246,15 @@ def main():
 
     dom = max((n for n in per if n != "reduce"), key=lambda n: per[n])
     kd = kernels[dom]
+    traffic = recorded_traffic(dom, args.workload, args.dtype)
     if kd["bound"] == "hbm":
         roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": kd["frac"], "traffic": None}
+                    "frac": kd["frac"], "traffic": traffic}
     else:
         roofline = {"kernel": dom, "bound": "mfma", "achieved": kd["TFLOP_s"], "peak": peak_t, "unit": "TFLOP/s",
-                    "frac": kd["frac"], "traffic": None}
+                    "frac": kd["frac"], "traffic": traffic}
+    for name in kernels:
+        kernels[name]["hbm_traffic_bytes"] = recorded_traffic(name, args.workload, args.dtype)
 
     filter_tbs = kernels["filter"]["GB_s"] / 1e3
     fwd_ms = per["fused_fwd"]
