@@ -8,8 +8,6 @@
 
 namespace {
 
-constexpr int64_t kMaxGridYZ = 65535;
-
 bool bad_ptr(const void *p, int dtype) {
     if (p == nullptr) return true;
     const uintptr_t a = (uintptr_t)p;
@@ -29,8 +27,6 @@ int check_shape(int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype) {
     const double elems = (double)N * 3.0 * (double)C * K * K * (double)H * (double)W;
     if (elems > 4.0e18) return DDPM_ERR_INVALID_ARG;
     if ((double)N * H * W >= 2147483648.0) return DDPM_ERR_INVALID_ARG;
-    // Launch-grid limit of the weight-gradient kernel (token splits x channel-block grid rows).
-    if (((C + 15) / 16) * ((C + 63) / 64) > kMaxGridYZ) return DDPM_ERR_UNSUPPORTED;
     return DDPM_OK;
 }
 

@@ -47,7 +47,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     L /= ncolt;
     const int h = (L % nbands) * kRows + wave;
     const int n = L / nbands;
-    if (h >= H) return;  // no barriers in this kernel
+    // bias slice: bl[(b*KK + t)*16 + ch] = bias[(b*C + c0 + ch)*KK + t]
+    __shared__ float bl[3 * KK * 16];
+    for (int i = threadIdx.x; i < 3 * KK * 16; i += blockDim.x) {
+        const int combo = i >> 4;
+        const int c = c0 + (i & 15);
+        const int b = combo / KK;
+        const int t = combo - b * KK;
+        bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+    }
+    __syncthreads();
+    if (h >= H) return;  // no barriers below
     const int64_t HW = (int64_t)H * W;
     const bool aligned4 = al != 0;
     const bool cvec = Elem<T>::is_bf16 ? (al != 0 && (C & 7) == 0) : (al != 0 && (C & 3) == 0);
@@ -59,7 +69,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     // Wave-uniform: all 16 channels exist, every weight chunk is whole and vector-aligned.
     // (KQ chunks must cover exactly C channels: the fp32 KQ=4 instance also serves C = 48;
     // the streamed KQ=0 instance only visits chunks q < nq.)
-    const bool full = (c0 + 16 <= C) && cvec && (C % G::CH == 0) && (KQ == 0 || KQ * G::CH == C);
+    // Fast paths also address a chunk as uniform base + 32-bit lane offset (< 32 planes).
+    const bool full = (c0 + 16 <= C) && cvec && (C % G::CH == 0) && (KQ == 0 || KQ * G::CH == C) &&
+                      HW < (int64_t(1) << 26);
+    const int HWi = (int)(full ? HW : 0);
+    const int aoff = cA * KK * C + (G::CH / 4) * g;  // lane's offset inside a (b, t) weight slice
 
     float dacc[4][4];
 #pragma unroll
@@ -88,8 +102,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
             // wave-uniform: the shifted row exists and all 64 shifted columns are inside it
             const int odd = dc & 1;
             if (full && rs_ok && w0 - dc - odd >= 0 && w0 + kCols - 1 - dc < W) {
-                st.a = G::load_A_fast(wg + ((int64_t)(b * C + cA) * KK + t) * C, q, g);
-                st.y = G::load_B_fast(yn, q, g, HW, rowoff, w - dc, aligned4 && ((dc & 3) == 0), aligned4, odd);
+                st.a = G::load_A_off(wg + ((int64_t)b * C * KK + t) * C, aoff + G::CH * q);
+                st.y = G::load_B_off(yn + (int64_t)(G::CH * q) * HW + rowoff, (G::CH / 4) * g * HWi + w - dc, HWi,
+                                     aligned4 && ((dc & 3) == 0), aligned4, odd);
             } else {
                 const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
                 st.a = G::load_A(arow, q, g, C, cvec);
@@ -107,21 +122,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
             const bool rs_ok = hs >= 0 && hs < H;
             const bool al_s = aligned4 && ((((kj - r) * D) & 3) == 0);
             const int64_t rowoff = (int64_t)(rs_ok ? hs : 0) * W;
-            float bias[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int c = c0 + 4 * g + v;
-                bias[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
-            }
             // G_b at the source pixels (consumed after the MFMAs)
             f32x4 gs[4];
             const int dcs = (kj - r) * D;
             const int odd = dcs & 1;
             if (full && rs_ok && w0 - dcs - odd >= 0 && w0 + kCols - 1 - dcs < W) {  // wave-uniform
+                const T *gbase = gn + (int64_t)((1 + b) * C + c0) * HW + rowoff;  // uniform
+                const int goff = 4 * g * HWi + ws;                                  // lane
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    gs[v] = load4_unchecked(gn + (int64_t)((1 + b) * C + c0 + 4 * g + v) * HW + rowoff, ws, al_s,
-                                            aligned4, odd);
+                    gs[v] = load4_unchecked(gbase + (int64_t)v * HWi, goff, al_s, aligned4, odd);
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -130,9 +140,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
                                       rs_ok && c < C, al_s);
                 }
             }
+            const f32x4 bias = *(const f32x4 *)(bl + (b * KK + t) * 16 + 4 * g);
             f32x4 acc[4];
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
+            for (int pb = 0; pb < 4; ++pb) acc[pb] = bias;
             if constexpr (KQ > 0) {
 #pragma unroll
                 for (int q = 0; q < KQ; ++q) {
@@ -262,12 +273,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
                 o.a[m] = (c_ok && cp < C) ? wrow[cp] : 0.f;
             }
         };
-        Ops nxt;
-        if (i0 < i1) fetch(i0, nxt);
+        // two items in flight ahead of the MFMAs
+        Ops n1, n2;
+        if (i0 < i1) fetch(i0, n1);
+        if (i0 + 1 < i1) fetch(i0 + 1, n2);
 #pragma unroll 1
         for (int i = i0; i < i1; ++i) {
-            const Ops cur = nxt;
-            if (i + 1 < i1) fetch(i + 1, nxt);
+            const Ops cur = n1;
+            n1 = n2;
+            if (i + 2 < i1) fetch(i + 2, n2);
 #pragma unroll
             for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -375,15 +389,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
 
 // ============================================================================ dW / db
 // One workgroup = CG generator (branch, tap) pairs x 16 depthwise channels x up to
-// 64 input channels c' of the weight gradient x one token split s.  The four waves
+// 64 input channels c' of the weight gradient x one token split s.  The kDwWaves waves
 // take interleaved chunks of the split's tokens and are summed in a fixed order
 // through LDS at the end, so each partial element is stored exactly once.
 //   MFMA rows    = channel c0 + i of one (b, t) pair (i = lane%16 as A supplier);
 //   MFMA columns = c' = cn0 + 16*nb + j (j = lane%16 as B supplier);
 //   contraction  = tokens: float32 4 per k-step (lane group g), four k-steps per
 //                  16-token chunk; bfloat16 32 per k-step (8 per lane group).
+constexpr int kDwWaves = 4;  // waves per dW workgroup; they split the token range
+
 template <typename T, int K, int CG, int NB>
-__global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, const T *__restrict__ y,
+__global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restrict__ x, const T *__restrict__ y,
                                                      const T *__restrict__ gout, float *__restrict__ dw_part,
                                                      float *__restrict__ db_part, int N, int C, int H, int W, int S) {
     constexpr int r = (K - 1) / 2;
@@ -392,19 +408,27 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
     constexpr bool BF = Elem<T>::is_bf16;
     constexpr int RL = BF ? 8 : 4;  // tokens per lane per chunk
     constexpr int KC = 4 * RL;      // tokens per wave per chunk
-    __shared__ float red[4][NB * 4][64];
-    __shared__ float redb[4][4][16];
+    __shared__ float red[kDwWaves][NB * 4][64];
+    __shared__ float redb[kDwWaves][4][16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int g = lane >> 4;
     const int j = lane & 15;
-    const int combo0 = blockIdx.x * CG;
+    // Logical order: (b, t) group fastest, then channel block x c' group, then split,
+    // laid out XCD-contiguously so the workgroups of one token split (which read the
+    // same y, x and G rows) share an L2.
+    const int nCG = (NCOMBO + CG - 1) / CG;
     const int nCB = (C + 15) >> 4;
-    const int cb = blockIdx.y % nCB;
+    const int nNG = (C + 63) >> 6;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int combo0 = (L % nCG) * CG;
+    L /= nCG;
+    const int cb = L % nCB;
+    L /= nCB;
     const int c0 = cb * 16;
-    const int cn0 = (blockIdx.y / nCB) * 64;
-    const int s = blockIdx.z;
+    const int cn0 = (L % nNG) * 64;
+    const int s = L / nNG;
     const int64_t HW = (int64_t)H * W;
     const int64_t CHW = (int64_t)C * HW;
     const int64_t ntok = (int64_t)N * HW;
@@ -583,8 +607,8 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
         }
     };
     auto advance = [&](int64_t &q0, int &qn, int &qh, int &qw) {
-        q0 += 4 * KC;
-        qw += 4 * KC;
+        q0 += kDwWaves * KC;
+        qw += kDwWaves * KC;
         while (qw >= W) {
             qw -= W;
             if (++qh == H) {
@@ -671,15 +695,16 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const T *__restrict__ x, co
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int c = c0 + 4 * g + v;
-                    const float sum = ((red[0][nb * 4 + v][lane] + red[1][nb * 4 + v][lane]) + red[2][nb * 4 + v][lane]) +
-                                      red[3][nb * 4 + v][lane];
+                    float sum = red[0][nb * 4 + v][lane];
+#pragma unroll
+                    for (int wv = 1; wv < kDwWaves; ++wv) sum += red[wv][nb * 4 + v][lane];  // fixed order
                     if (c < C && cp < C) dwp[((int64_t)(b * C + c) * KK + t) * C + cp] = sum;
                 }
             }
             if (wave == 0 && g == 0 && cn0 == 0 && cA_ok) {
                 float sb = 0.f;
 #pragma unroll
-                for (int wv = 0; wv < 4; ++wv)
+                for (int wv = 0; wv < kDwWaves; ++wv)
 #pragma unroll
                     for (int gg = 0; gg < 4; ++gg) sb += redb[wv][gg][j];
                 dbp[(int64_t)(b * C + cA) * KK + t] = sb;
@@ -736,10 +761,10 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
         // pairs keep the prefetched operands inside the register budget.
         constexpr int CG = Elem<T>::is_bf16 ? 2 : 4;
         constexpr int NCOMBO = 3 * K * K;
-        dim3 grid((NCOMBO + CG - 1) / CG, ((C + 15) / 16) * ((C + 63) / 64), S);
+        const dim3 grid((unsigned)(((NCOMBO + CG - 1) / CG) * ((C + 15) / 16) * ((C + 63) / 64) * S));
         const int nb = (C >= 64) ? 4 : (C + 15) / 16;
         auto args = [&](auto kern) {
-            hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)x, (const T *)y, (const T *)gout, dwp, dbp,
+            hipLaunchKernelGGL(kern, grid, dim3(64 * kDwWaves), 0, stream, (const T *)x, (const T *)y, (const T *)gout, dwp, dbp,
                                N, C, H, W, S);
         };
         if (nb == 1) args(bwd_dw_kernel<T, K, CG, 1>);

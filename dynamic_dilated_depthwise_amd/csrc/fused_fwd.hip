@@ -28,7 +28,8 @@ template <int K> struct XTile {
     static constexpr int LH = kTileRows + 2 * HALO;
     static constexpr int LW = kTileCols + 2 * HALO;
     static constexpr int PLANE = LH * LW;
-    static constexpr size_t bytes = sizeof(float) * 16 * PLANE;
+    static constexpr int BIAS = 3 * K * K * 16;  // bias of the 16 channels for every (b, t)
+    static constexpr size_t bytes = sizeof(float) * (16 * PLANE + BIAS);
 };
 
 // Stage x[n, c0..c0+15, h0-HALO .., w0-HALO ..] into LDS as float, zero outside.
@@ -82,6 +83,15 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const T *__restrict__ xn = x + (int64_t)n * C * HW;
     const T *__restrict__ yn = y + (int64_t)n * C * HW;
     stage_x_tile<T, K>(xs, xn, c0, C, H, W, HW, h0, w0);
+    // bias slice: bl[(b*KK + t)*16 + ch] = bias[(b*C + c0 + ch)*KK + t]
+    float *bl = xs + 16 * X::PLANE;
+    for (int i = threadIdx.x; i < X::BIAS; i += blockDim.x) {
+        const int combo = i >> 4;
+        const int c = c0 + (i & 15);
+        const int b = combo / KK;
+        const int t = combo - b * KK;
+        bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+    }
 
     const int h = h0 + wave;
     const bool row_ok = h < H;
@@ -108,58 +118,41 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) oacc[b][v][pb] = 0.f;
 
+    const int aoff = cA * KK * C + 4 * (Elem<T>::is_bf16 ? 2 : 1) * g;  // lane's offset inside a (b, t) slice
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
         const int D = dilation(b);
-        // Generator-row operand and bias of tap t of this branch.
-        auto fetch = [&](int t, typename G::AFrag (&af)[KQ > 0 ? KQ : 1], float (&bf)[4]) {
+        // Generator-row operand of tap t of this branch.
+        auto fetch = [&](int t, typename G::AFrag (&af)[KQ > 0 ? KQ : 1]) {
             if (full) {  // wave-uniform: every row and column exists
-                const T *arow = wg + ((int64_t)(b * C + cA) * KK + t) * C;
+                // uniform slice base + 32-bit lane offset
+                const T *wbt = wg + ((int64_t)b * C * KK + t) * C;
 #pragma unroll
-                for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) af[q] = G::load_A_fast(arow, q, g);
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    bf[v] = Elem<T>::to_f32(bg[(int64_t)(b * C + c0 + 4 * g + v) * KK + t]);
+                for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) af[q] = G::load_A_off(wbt, aoff + G::CH * q);
                 return;
             }
             const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
 #pragma unroll
             for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) af[q] = G::load_A(arow, q, g, C, cvec);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int c = c0 + 4 * g + v;
-                bf[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
-            }
         };
         typename G::AFrag anext[KQ > 0 ? KQ : 1];
-        float bnext[4];
-        if constexpr (KQ > 0) fetch(0, anext, bnext);
+        if constexpr (KQ > 0) fetch(0, anext);
 #pragma unroll 1
         for (int t = 0; t < KK; ++t) {
+            const f32x4 bias = *(const f32x4 *)(bl + (b * KK + t) * 16 + 4 * g);
             f32x4 acc[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc[pb] = bias;
             if constexpr (KQ > 0) {
                 // operands of tap t were fetched one tap ahead; fetch tap t+1 now
                 typename G::AFrag acur[KQ];
-                float bcur[4];
 #pragma unroll
                 for (int q = 0; q < KQ; ++q) acur[q] = anext[q];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) bcur[v] = bnext[v];
-                if (t + 1 < KK) fetch(t + 1, anext, bnext);
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bcur[0], bcur[1], bcur[2], bcur[3]};
+                if (t + 1 < KK) fetch(t + 1, anext);
 #pragma unroll
                 for (int q = 0; q < KQ; ++q) G::mma(acc, acur[q], bres[q]);
             } else {
                 const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
-                float bias[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int c = c0 + 4 * g + v;
-                    bias[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
-                }
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{bias[0], bias[1], bias[2], bias[3]};
                 for (int q = 0; q < nq; ++q)
                     G::mma(acc, G::load_A(arow, q, g, C, cvec),
                            G::load_B(yn, q, g, C, HW, rowoff, w, W, row_ok, aligned4));

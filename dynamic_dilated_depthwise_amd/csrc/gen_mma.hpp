@@ -51,6 +51,21 @@ template <> struct Gen<float> {
             b.v[s] = load4_unchecked(yn + (int64_t)(16 * q + 4 * g + s) * HW + rowoff, w, w_al, true, false);
         return b;
     }
+    // Fragment at a wave-uniform base plus a 32-bit lane offset (16-byte aligned).
+    __device__ __forceinline__ static AFrag load_A_off(const float *__restrict__ base, int off) {
+        AFrag a;
+        a.v = *(const f32x4 *)(base + off);
+        return a;
+    }
+    // load_B_fast addressed as a wave-uniform row base of the chunk's first channel
+    // plus a 32-bit lane offset (lane group g's plane and column); planes HW apart.
+    __device__ __forceinline__ static BFrag load_B_off(const float *__restrict__ base, int off, int HW, bool w_al,
+                                                       bool, bool) {
+        BFrag b;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b.v[s] = load4_unchecked(base + (int64_t)s * HW, off, w_al, true, false);
+        return b;
+    }
     // As load_A for an existing row with C % 4 == 0 and a 16-byte aligned weight.
     __device__ __forceinline__ static AFrag load_A_fast(const float *__restrict__ arow, int q, int g) {
         AFrag a;
@@ -152,6 +167,26 @@ template <> struct Gen<bf16_t> {
             b.v[pb] = pack_bf16x8(col);
         }
         return b;
+    }
+    __device__ __forceinline__ static BFrag load_B_off(const bf16_t *__restrict__ base, int off, int HW, bool w_al,
+                                                       bool row_even, bool odd) {
+        uint16_t v[8][4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) load4_raw_fast(base + (int64_t)e * HW, off, w_al, row_even, odd, v[e]);
+        BFrag b;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            uint16_t col[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) col[e] = v[e][pb];
+            b.v[pb] = pack_bf16x8(col);
+        }
+        return b;
+    }
+    __device__ __forceinline__ static AFrag load_A_off(const bf16_t *__restrict__ base, int off) {
+        AFrag a;
+        a.v = __builtin_bit_cast(bf16x8, *(const u16x8 *)(base + off));
+        return a;
     }
     // As load_A for an existing row with C % 8 == 0 and a 16-byte aligned weight.
     __device__ __forceinline__ static AFrag load_A_fast(const bf16_t *__restrict__ arow, int q, int g) {
