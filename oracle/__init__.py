@@ -10,7 +10,7 @@ this module only marshals numpy arrays into it.  What is computed follows the pa
 "lartpang/DynamicConvolutionOperator" (DDPM from HDFNet, ECCV 2020): the unfold
 definition named there as the mathematical reference ("Dynamic Convolution
 Operator" intro, "问题与目标"), the dilation set (1, 3, 5) and the output order
-[x, d1, d3, d5] ("CUDA 动态过滤"), the 1x1 generator ("CUDA 融合生成器推理") and the
+[x, d1, d3, d5] and the filter's dX / dK backward ("CUDA 动态过滤"), the 1x1 generator ("CUDA 融合生成器推理") and the
 training adjoints ("CUDA Flash 式融合训练").
 
 Every function takes and returns float64 arrays in NCHW layout:
@@ -54,8 +54,9 @@ def load(path=_LIB):
     lib.ddpm_oracle_fused_fwd.argtypes = [_D, _D, _D, _D, _D, _I64, _I64, _I64, _I64, ctypes.c_int]
     lib.ddpm_oracle_fused_bwd.argtypes = [_D] * 9 + [_I64, _I64, _I64, _I64, ctypes.c_int]
     lib.ddpm_oracle_sum_partials.argtypes = [_D, _D, _I64, _I64]
+    lib.ddpm_oracle_filter_bwd.argtypes = [_D] * 5 + [_I64, _I64, _I64, _I64, ctypes.c_int]
     for f in ("ddpm_oracle_generator", "ddpm_oracle_filter_fwd", "ddpm_oracle_fused_fwd",
-              "ddpm_oracle_fused_bwd", "ddpm_oracle_sum_partials"):
+              "ddpm_oracle_fused_bwd", "ddpm_oracle_sum_partials", "ddpm_oracle_filter_bwd"):
         getattr(lib, f).restype = None
     return lib
 
@@ -124,6 +125,16 @@ class Oracle:
         self.lib.ddpm_oracle_fused_bwd(_p(x), _p(y), _p(Wg), _p(bg), _p(G), _p(dx), _p(dy),
                                        _p(dWg), _p(dbg), N, C, H, W, K)
         return dx, dy, dWg, dbg
+
+    def filter_bwd(self, x, taps, G, K):
+        """Returns (dx, dtaps) for L = <G, filter_fwd(x, taps)>."""
+        x, taps, G = _arr(x), _arr(taps), _arr(G)
+        N, C, H, W = x.shape
+        assert taps.shape == (N, 3 * C * K * K, H, W) and G.shape == (N, 4 * C, H, W)
+        dx = np.empty_like(x)
+        dtaps = np.empty_like(taps)
+        self.lib.ddpm_oracle_filter_bwd(_p(x), _p(taps), _p(G), _p(dx), _p(dtaps), N, C, H, W, K)
+        return dx, dtaps
 
     def sum_partials(self, partials):
         partials = _arr(partials)

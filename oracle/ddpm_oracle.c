@@ -311,6 +311,51 @@ void ddpm_oracle_fused_bwd(const double *x, const double *y, const double *Wg, c
 }
 
 /*
+ * Backward of the materialised filter ("CUDA 动态过滤": the backward produces dX and
+ * dK, the gradient of the dynamic kernels).  With G = dL/d out:
+ *   dtaps[n,o,p] = G_b[n,c,p] * x[n,c,p+delta_{b,t}]            (zero outside)
+ *   dx[n,c,q]    = G_x[n,c,q] + sum_{b,t,p : p+delta=q} taps[n,o,p] * G_b[n,c,p]
+ * dx is formed by scattering each source pixel's contribution, as in the fused
+ * backward above.
+ */
+void ddpm_oracle_filter_bwd(const double *x, const double *taps, const double *G, double *dx, double *dtaps,
+                            int64_t N, int64_t C, int64_t H, int64_t W, int K)
+{
+    const int64_t R = 3 * C * K * K;
+    const int64_t HW = H * W;
+    const int r = (K - 1) / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t nc = 0; nc < N * C; ++nc) {
+        const int64_t n = nc / C, c = nc % C;
+        double *dxp = dx + (n * C + c) * HW;
+        const double *Gx = G + (n * 4 * C + c) * HW;
+        for (int64_t q = 0; q < HW; ++q)
+            dxp[q] = Gx[q];
+        for (int b = 0; b < 3; ++b) {
+            const int D = DILATION[b];
+            const double *Gb = G + (n * 4 * C + (1 + b) * C + c) * HW;
+            for (int ki = 0; ki < K; ++ki) {
+                for (int kj = 0; kj < K; ++kj) {
+                    const int64_t o = gen_row(b, c, ki * K + kj, C, K);
+                    const double *tp = taps + (n * R + o) * HW;
+                    double *dtp = dtaps + (n * R + o) * HW;
+                    for (int64_t h = 0; h < H; ++h) {
+                        for (int64_t w = 0; w < W; ++w) {
+                            const int64_t hh = h + (int64_t)(ki - r) * D;
+                            const int64_t ww = w + (int64_t)(kj - r) * D;
+                            const int inside = hh >= 0 && hh < H && ww >= 0 && ww < W;
+                            dtp[h * W + w] = inside ? Gb[h * W + w] * x[((n * C + c) * H + hh) * W + ww] : 0.0;
+                            if (inside)
+                                dxp[hh * W + ww] += tp[h * W + w] * Gb[h * W + w];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+/*
  * Sum of per-split fp32 partials, in ascending split order, in double.
  * partial[s][m] for s < S, m < M  ->  sum[m].
  */

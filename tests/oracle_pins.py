@@ -248,6 +248,82 @@ def pin_autograd_unfold(o):
             _close(g, t.grad.numpy(), 1e-12, f"autograd {name} {N,C,H,W,K}")
 
 
+def torch_unfold_filter(x, taps, K):
+    """The page's construction with materialised taps: three Unfold(x) times the taps."""
+    N, C, H, W = x.shape
+    r = (K - 1) // 2
+    T = taps.reshape(N, 3, C, K * K, H, W)
+    outs = [x]
+    for bi, D in enumerate(DILATIONS):
+        U = F.unfold(x, K, dilation=D, padding=D * r).reshape(N, C, K * K, H, W)
+        outs.append((U * T[:, bi]).sum(2))
+    return torch.cat(outs, 1)
+
+
+def numpy_brute_dtaps(x, G, K):
+    """dK[o, p] = G_b[c, p] * x[c, p + delta] by zero padding and slicing."""
+    N, C, H, W = x.shape
+    r = (K - 1) // 2
+    P = 5 * r
+    xp = np.zeros((N, C, H + 2 * P, W + 2 * P))
+    xp[:, :, P:P + H, P:P + W] = x
+    out = np.zeros((N, 3, C, K, K, H, W))
+    for bi, D in enumerate(DILATIONS):
+        Gb = G[:, (1 + bi) * C:(2 + bi) * C]
+        for ki in range(K):
+            for kj in range(K):
+                dh, dw = (ki - r) * D, (kj - r) * D
+                out[:, bi, :, ki, kj] = Gb * xp[:, :, P + dh:P + dh + H, P + dw:P + dw + W]
+    return out.reshape(N, 3 * C * K * K, H, W)
+
+
+def pin_filter_bwd_brute_and_autograd(o):
+    rng = np.random.default_rng(22)
+    for (N, C, H, W, K) in [(2, 5, 15, 17, 3), (1, 3, 9, 8, 5), (1, 4, 6, 7, 1), (1, 2, 1, 1, 3)]:
+        x = rng.standard_normal((N, C, H, W))
+        taps = rng.standard_normal((N, 3 * C * K * K, H, W))
+        G = rng.standard_normal((N, 4 * C, H, W))
+        dx, dtaps = o.filter_bwd(x, taps, G, K)
+        _close(dtaps, numpy_brute_dtaps(x, G, K), 1e-14, f"dtaps brute {N,C,H,W,K}")
+        xt = torch.from_numpy(x.copy()).requires_grad_(True)
+        tt = torch.from_numpy(taps.copy()).requires_grad_(True)
+        (torch_unfold_filter(xt, tt, K) * torch.from_numpy(G)).sum().backward()
+        _close(dx, xt.grad.numpy(), 1e-12, f"filter dx autograd {N,C,H,W,K}")
+        _close(dtaps, tt.grad.numpy(), 1e-12, f"filter dtaps autograd {N,C,H,W,K}")
+
+
+def pin_filter_bwd_finite_differences_and_adjoint(o):
+    rng = np.random.default_rng(23)
+    N, C, H, W, K = 2, 4, 10, 13, 3
+    x = rng.standard_normal((N, C, H, W))
+    taps = rng.standard_normal((N, 3 * C * K * K, H, W))
+    G = rng.standard_normal((N, 4 * C, H, W))
+    dx, dtaps = o.filter_bwd(x, taps, G, K)
+    # L = <G, out> is linear in x alone and in taps alone: central differences are exact
+    for name, val, grad in (("x", x, dx), ("taps", taps, dtaps)):
+        v = rng.standard_normal(val.shape)
+        def loss(a):
+            return float((o.filter_fwd(a if name == "x" else x, a if name == "taps" else taps, K) * G).sum())
+        fd = (loss(val + 0.5 * v) - loss(val - 0.5 * v)) / 1.0
+        an = float((grad * v).sum())
+        assert abs(fd - an) <= 1e-9 * max(abs(fd), 1.0), f"filter FD {name}: {fd} vs {an}"
+    v = rng.standard_normal(x.shape)
+    lhs = float(((dx - G[:, :C]) * v).sum())
+    rhs = float((G[:, C:] * o.filter_fwd(v, taps, K)[:, C:]).sum())
+    assert abs(lhs - rhs) <= 1e-11 * max(abs(rhs), 1.0), f"filter adjoint {lhs} vs {rhs}"
+
+
+def pin_filter_bwd_matches_fused_bwd(o):
+    """With taps = generator(y), the filter's dX equals the fused backward's dX."""
+    rng = np.random.default_rng(24)
+    N, C, H, W, K = 1, 3, 11, 9, 3
+    x, y, Wg, bg = _rand_case(rng, N, C, H, W, K)
+    G = rng.standard_normal((N, 4 * C, H, W))
+    dx_f, _ = o.filter_bwd(x, o.generator(y, Wg, bg, K), G, K)
+    dx_u, _, _, _ = o.fused_bwd(x, y, Wg, bg, G, K)
+    _close(dx_f, dx_u, 1e-12, "filter dx vs fused dx")
+
+
 def pin_sum_partials(o):
     rng = np.random.default_rng(21)
     p = rng.standard_normal((16, 27, 8))
@@ -267,5 +343,8 @@ ALL_PINS = [
     pin_finite_differences,
     pin_adjoint_dx,
     pin_autograd_unfold,
+    pin_filter_bwd_brute_and_autograd,
+    pin_filter_bwd_finite_differences_and_adjoint,
+    pin_filter_bwd_matches_fused_bwd,
     pin_sum_partials,
 ]

@@ -38,6 +38,13 @@ MUTANTS = [
      "wrow[ci] += dk * y[((n * C + ci) * H + hh) * W + ww];", 0),
     ("db_sums_grad", "sb += dk;", "sb += G[((n * 4 * C + (1 + b) * C + c) * H + h) * W + w];", 0),
     ("partials_skip_last", "for (int64_t s = 0; s < S; ++s)", "for (int64_t s = 0; s + 1 < S; ++s)", 0),
+    ("filter_bwd_dtaps_unshifted_x", "Gb[h * W + w] * x[((n * C + c) * H + hh) * W + ww]",
+     "Gb[h * W + w] * x[((n * C + c) * H + h) * W + w]", 0),
+    ("filter_bwd_dx_missing_passthrough", "dxp[q] = Gx[q];", "dxp[q] = 0.0;", 1),
+    ("filter_bwd_dx_tap_at_destination", "dxp[hh * W + ww] += tp[h * W + w] * Gb[h * W + w];",
+     "dxp[hh * W + ww] += tp[hh * W + ww] * Gb[h * W + w];", 0),
+    ("filter_bwd_wrong_grad_block", "const double *Gb = G + (n * 4 * C + (1 + b) * C + c) * HW;",
+     "const double *Gb = G + (n * 4 * C + b * C + c) * HW;", 0),
 ]
 
 
