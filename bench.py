@@ -11,6 +11,8 @@ One step is one pass of the whole hot path over one batch of synthetic input
   4. ddpm_fused_bwd (dY)   on-chip dK contracted with the generator weight
   5. ddpm_fused_bwd (dW)   on-chip dK reduced into 16 float32 token partials
   6. ddpm_reduce_partials  fixed-order sum of the partials
+The backward of the materialised filter (ddpm_filter_bwd: dX and the tap
+gradient) is timed the same way right after the steps, outside ms_per_step.
 Each library call runs one kernel (the reduce runs two short ones), so HIP events
 recorded around every call on the launch stream give per-kernel durations over
 the timed region.  All inputs are resident in HBM before timing starts.
@@ -62,15 +64,18 @@ def algorithmic(shape, dtype_bytes, S):
         "bwd_dw": {"bytes": 5 * C * s * P + S * (R * C + R) * 4, "flops": gemm},
         # partials read, gradients written
         "reduce": {"bytes": S * (R * C + R) * 4 + (R * C + R) * s, "flops": 0.0},
+        # materialised backward: x, taps, G (4C) read, dX and dtaps written
+        "filter_bwd": {"bytes": (2 * R + 6 * C) * s * P, "flops": 2.0 * (2 * R + C) * P},
     }
 
 
 KERNEL_BOUND = {"filter": "hbm", "fused_fwd": "mfma", "bwd_dx": "mfma", "bwd_dy": "mfma", "bwd_dw": "mfma",
-                "reduce": "hbm"}
+                "reduce": "hbm", "filter_bwd": "hbm"}
 
 # Kernel symbol and the source files that define it (for the traffic record's digest).
 KERNEL_SYMBOL = {"filter": "filter_fwd_kernel", "fused_fwd": "fused_fwd_kernel", "bwd_dx": "bwd_dx_kernel",
-                 "bwd_dy": "bwd_dy_kernel", "bwd_dw": "bwd_dw_kernel", "reduce": "reduce_partials_kernel"}
+                 "bwd_dy": "bwd_dy_kernel", "bwd_dw": "bwd_dw_kernel", "reduce": "reduce_partials_kernel",
+                 "filter_bwd": "filter_bwd_kernel"}
 KERNEL_SOURCES = {
     "filter": ["filter_fwd.hip", "common.hpp"],
     "fused_fwd": ["fused_fwd.hip", "gen_mma.hpp", "common.hpp"],
@@ -78,6 +83,7 @@ KERNEL_SOURCES = {
     "bwd_dy": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dw": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
     "reduce": ["reduce.hip", "common.hpp"],
+    "filter_bwd": ["filter_bwd.hip", "common.hpp"],
 }
 CSRC = os.path.join(ROOT, "dynamic_dilated_depthwise_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -169,6 +175,8 @@ def main():
     pb = torch.empty((S, R), device="cuda", dtype=torch.float32)
     gw = torch.empty((R, C), device="cuda", dtype=dtype)
     gb = torch.empty((R,), device="cuda", dtype=dtype)
+    gx_f = torch.empty_like(d["x"])
+    gk_f = torch.empty_like(d["taps"])
     stream = torch.cuda.current_stream()
 
     calls = [
@@ -181,6 +189,11 @@ def main():
         ("bwd_dw", lambda: ddpm.ddpm_fused_bwd(d["x"], d["y"], d["weight"], d["bias"], d["grad_out"], None, None,
                                                pw, pb, K, stream)),
         ("reduce", lambda: ddpm.ddpm_reduce_partials(pw, pb, gw, gb, K, stream)),
+    ]
+    # Timed beside the step, not inside it: the backward of the materialised filter
+    # (dX and dtaps from the taps), the training counterpart of call 1.
+    extra_calls = [
+        ("filter_bwd", lambda: ddpm.ddpm_filter_bwd(d["x"], d["taps"], d["grad_out"], gx_f, gk_f, K, stream)),
     ]
 
     def step(events=None):
@@ -230,6 +243,20 @@ def main():
            for i, (name, _) in enumerate(calls)}
     log("per-call ms " + " ".join(f"{k}={v:.4f}" for k, v in per.items()))
 
+    for name, fn in extra_calls:
+        for _ in range(args.warmup):
+            fn()
+        xev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in xev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per[name] = sum(e0.elapsed_time(e1) for e0, e1 in xev) / args.steps
+        log(f"{name} (outside the step) ms={per[name]:.4f}")
+
     alg = algorithmic(shape, es, S)
     peak_t = MFMA_PEAK_TFLOPS[args.dtype]
     kernels = {}
@@ -242,9 +269,10 @@ def main():
             "ms": round(ms, 5), "bound": kb, "alg_bytes": int(a["bytes"]), "alg_flops": a["flops"],
             "GB_s": round(gbs, 1), "TFLOP_s": round(tfl, 2),
             "frac": round(gbs / HBM_PEAK_GBS if kb == "hbm" else tfl / peak_t, 4),
+            "in_step": name not in dict(extra_calls),
         }
 
-    dom = max((n for n in per if n != "reduce"), key=lambda n: per[n])
+    dom = max((n for n, _ in calls if n != "reduce"), key=lambda n: per[n])
     kd = kernels[dom]
     traffic = recorded_traffic(dom, args.workload, args.dtype)
     if kd["bound"] == "hbm":

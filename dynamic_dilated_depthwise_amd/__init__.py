@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "DDPMError",
     "ddpm_filter_fwd",
+    "ddpm_filter_bwd",
     "ddpm_fused_fwd",
     "ddpm_fused_bwd",
     "ddpm_reduce_partials",
@@ -63,10 +64,11 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.ddpm_filter_fwd.argtypes = [P, P, P, I64, I64, I64, I64, I, I, P]
+    lib.ddpm_filter_bwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I, I, P]
     lib.ddpm_fused_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I, I, P]
     lib.ddpm_fused_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I64, I64, I64, I64, I, I, P]
     lib.ddpm_reduce_partials.argtypes = [P, P, I, P, P, I64, I, I, P]
-    for f in ("ddpm_filter_fwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials"):
+    for f in ("ddpm_filter_fwd", "ddpm_filter_bwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials"):
         getattr(lib, f).restype = I
     lib.ddpm_status_string.argtypes = [I]
     lib.ddpm_status_string.restype = ctypes.c_char_p
@@ -127,6 +129,20 @@ def ddpm_filter_fwd(x, taps, out, K, stream=None):
     dt = x.dtype
     args = (_dev(x, "x", dt), _dev(taps, "taps", dt, (N, R, H, W)), _dev(out, "out", dt, (N, 4 * C, H, W)))
     _check("ddpm_filter_fwd", _load().ddpm_filter_fwd(*args, N, C, H, W, K, _dtype_code(x), _stream(stream)))
+
+
+def ddpm_filter_bwd(x, taps, grad_out, grad_x, grad_taps, K, stream=None):
+    """grad_x and / or grad_taps of the materialised filter (see include/ddpm.h);
+    either output may be None to skip it."""
+    N, C, H, W = x.shape
+    R = 3 * C * K * K
+    dt = x.dtype
+    null = ctypes.c_void_p(None)
+    args = (_dev(x, "x", dt), _dev(taps, "taps", dt, (N, R, H, W)),
+            _dev(grad_out, "grad_out", dt, (N, 4 * C, H, W)),
+            null if grad_x is None else _dev(grad_x, "grad_x", dt, (N, C, H, W)),
+            null if grad_taps is None else _dev(grad_taps, "grad_taps", dt, (N, R, H, W)))
+    _check("ddpm_filter_bwd", _load().ddpm_filter_bwd(*args, N, C, H, W, K, _dtype_code(x), _stream(stream)))
 
 
 def ddpm_fused_fwd(x, y, weight, bias, out, K, stream=None):

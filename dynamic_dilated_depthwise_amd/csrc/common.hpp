@@ -257,6 +257,32 @@ template <> struct RowRun<bf16_t, 8> {
     }
 };
 
+// VEC consecutive elements of a row as one vector register value (VEC = 1: scalar).
+template <typename T, int VEC> struct VecOf;
+template <> struct VecOf<float, 4> { typedef float type __attribute__((ext_vector_type(4))); };
+template <> struct VecOf<float, 2> { typedef float type __attribute__((ext_vector_type(2))); };
+template <> struct VecOf<float, 1> { typedef float type; };
+template <> struct VecOf<bf16_t, 8> { typedef uint16_t type __attribute__((ext_vector_type(8))); };
+template <> struct VecOf<bf16_t, 4> { typedef uint16_t type __attribute__((ext_vector_type(4))); };
+template <> struct VecOf<bf16_t, 2> { typedef uint16_t type __attribute__((ext_vector_type(2))); };
+template <> struct VecOf<bf16_t, 1> { typedef uint16_t type; };
+
+template <typename V, typename T, int VEC>
+__device__ __forceinline__ T lane_of(const V &v, int k) {
+    if constexpr (VEC == 1) return v; else return v[k];
+}
+template <typename V, typename T, int VEC>
+__device__ __forceinline__ void set_lane(V &v, int k, T val) {
+    if constexpr (VEC == 1) v = val; else v[k] = val;
+}
+
+// Exact narrowing of a value that was widened from T (used for the x copy).
+template <typename T> __device__ __forceinline__ T exact_narrow(float v);
+template <> __device__ __forceinline__ float exact_narrow<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t exact_narrow<bf16_t>(float v) {
+    return (bf16_t)(__float_as_uint(v) >> 16);
+}
+
 // Raw (bit-exact) copy helpers for the x block of the output.
 template <typename T>
 __device__ __forceinline__ void copy4_row(const T *__restrict__ src, T *__restrict__ dst, int w, int W,

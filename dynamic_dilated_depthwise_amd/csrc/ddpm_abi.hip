@@ -74,6 +74,44 @@ int ddpm_filter_fwd(const void *x, const void *taps, void *out, int64_t N, int64
     return status_of(ddpm::launch_filter_fwd(x, taps, out, (int)N, (int)C, (int)H, (int)W, K, bf16, vec, stream));
 }
 
+int ddpm_filter_bwd(const void *x, const void *taps, const void *grad_out, void *grad_x, void *grad_taps, int64_t N,
+                    int64_t C, int64_t H, int64_t W, int K, int dtype, hipStream_t stream) {
+    int st = check_shape(N, C, H, W, K, dtype);
+    if (st != DDPM_OK) return st;
+    if (bad_ptr(x, dtype) || bad_ptr(taps, dtype) || bad_ptr(grad_out, dtype)) return DDPM_ERR_INVALID_ARG;
+    if (grad_x == nullptr && grad_taps == nullptr) return DDPM_ERR_INVALID_ARG;
+    if ((grad_x != nullptr && bad_ptr(grad_x, dtype)) || (grad_taps != nullptr && bad_ptr(grad_taps, dtype)))
+        return DDPM_ERR_INVALID_ARG;
+    const int64_t es = dtype == DDPM_BF16 ? 2 : 4;
+    const int64_t HW = H * W;
+    const int64_t R = 3 * C * K * K;
+    const int64_t xb = N * C * HW * es, tb = N * R * HW * es, gb = N * 4 * C * HW * es;
+    const void *ins[3] = {x, taps, grad_out};
+    const int64_t inb[3] = {xb, tb, gb};
+    void *outs[2] = {grad_x, grad_taps};
+    const int64_t outb[2] = {xb, tb};
+    for (int o = 0; o < 2; ++o) {
+        if (outs[o] == nullptr) continue;
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(outs[o], outb[o], ins[i], inb[i])) return DDPM_ERR_INVALID_ARG;
+    }
+    if (grad_x != nullptr && grad_taps != nullptr && overlaps(grad_x, xb, grad_taps, tb)) return DDPM_ERR_INVALID_ARG;
+    const bool bf16 = dtype == DDPM_BF16;
+    int vec = 1;
+    for (int v = bf16 ? 8 : 4; v > 1; v /= 2) {
+        const uintptr_t a = (uintptr_t)v * es;
+        if (W % v == 0 && (grad_x == nullptr || (uintptr_t)grad_x % a == 0) &&
+            (grad_taps == nullptr || (uintptr_t)grad_taps % a == 0)) {
+            vec = v;
+            break;
+        }
+    }
+    const bool al = (W % 4) == 0 && aligned16(taps);
+    (void)hipGetLastError();
+    return status_of(ddpm::launch_filter_bwd(x, taps, grad_out, grad_x, grad_taps, (int)N, (int)C, (int)H, (int)W, K,
+                                             bf16, vec, al, stream));
+}
+
 int ddpm_fused_fwd(const void *x, const void *y, const void *weight, const void *bias, void *out, int64_t N,
                    int64_t C, int64_t H, int64_t W, int K, int dtype, hipStream_t stream) {
     int st = check_shape(N, C, H, W, K, dtype);

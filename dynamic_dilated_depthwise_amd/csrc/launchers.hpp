@@ -20,6 +20,10 @@ hipError_t launch_fused_bwd(const void *x, const void *y, const void *wg, const 
                             void *gx, void *gy, float *dw_part, float *db_part, int S, int N, int C, int H,
                             int W, int K, bool bf16, bool aligned4, hipStream_t stream);
 
+// gx or gtaps may be null: that output is skipped (not both).
+hipError_t launch_filter_bwd(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N, int C,
+                             int H, int W, int K, bool bf16, int vec, bool aligned, hipStream_t stream);
+
 hipError_t launch_reduce_partials(const float *dw_part, const float *db_part, int S, void *gw, void *gb,
                                   int64_t R, int C, bool bf16, hipStream_t stream);
 

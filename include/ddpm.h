@@ -88,6 +88,24 @@ int ddpm_filter_fwd(const void *x, const void *taps, void *out,
                     hipStream_t stream);
 
 /*
+ * ddpm_filter_bwd -- backward of the materialised filter (page section
+ * "CUDA 动态过滤": the backward fuses dX and dK, the gradient of the dynamic
+ * kernels, with no patch matrix).  With G = grad_out = [G_x, G_0, G_1, G_2]:
+ *   grad_taps[n, o(b,c,t), p] = G_b[n, c, p] * x[n, c, p + d_bt]   (zero outside)
+ *   grad_x[n, c, q] = G_x[n, c, q] + sum_{b,t} taps[n, o, q - d_bt] * G_b[n, c, q - d_bt]
+ *
+ *   x         [N, C, H, W]            in   dtype
+ *   taps      [N, 3*C*K*K, H, W]      in   dtype
+ *   grad_out  [N, 4*C, H, W]          in   dtype
+ *   grad_x    [N, C, H, W]            out  dtype, or NULL (not computed)
+ *   grad_taps [N, 3*C*K*K, H, W]      out  dtype, or NULL (not computed)
+ * At least one output must be requested (else DDPM_ERR_INVALID_ARG).  bfloat16
+ * outputs are rounded once from float32 products and sums.
+ */
+int ddpm_filter_bwd(const void *x, const void *taps, const void *grad_out, void *grad_x, void *grad_taps,
+                    int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype, hipStream_t stream);
+
+/*
  * ddpm_fused_fwd -- generator fused with the filter (page section
  * "CUDA 融合生成器推理": weight x y-tile -> taps -> consumed with shifted x; the
  * taps never reach global memory).

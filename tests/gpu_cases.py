@@ -4,7 +4,9 @@ fp64 oracle on the same seeded inputs, and compare.
 Tolerances (error = max|gpu - oracle| / max|oracle|, per tensor):
   float32   outputs 2e-4, gradients 1e-3
   bfloat16  outputs and gradients 2e-2
-The x block of every forward output must equal x bit for bit.
+The x block of every forward output must equal x bit for bit, and so must every
+element of the materialised-filter tap gradient (one product of two inputs, exact
+in fp64 and rounded once on either side).
 """
 import sys
 
@@ -94,3 +96,12 @@ def gpu_bwd(d, K, S=None):
     ddpm.ddpm_reduce_partials(pw, pb, gw, gb, K)
     torch.cuda.synchronize()
     return gx, gy, gw, gb, pw, pb
+
+
+def gpu_filter_bwd(d, K, want_dx=True, want_dk=True):
+    x, taps = d["x"], d["taps"]
+    gx = torch.empty_like(x) if want_dx else None
+    gk = torch.empty_like(taps) if want_dk else None
+    ddpm.ddpm_filter_bwd(x, taps, d["grad_out"], gx, gk, K)
+    torch.cuda.synchronize()
+    return gx, gk

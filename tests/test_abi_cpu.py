@@ -36,7 +36,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "ddpm_filter_fwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials", "ddpm_status_string"])
+        "ddpm_filter_fwd", "ddpm_filter_bwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials",
+        "ddpm_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -68,6 +69,10 @@ def _filter(lib, x=A, taps=B, out=Cp, N=1, C=8, H=16, W=16, K=3, dt=F32):
     return lib.ddpm_filter_fwd(x, taps, out, N, C, H, W, K, dt, None)
 
 
+def _filter_bwd(lib, x=A, taps=B, g=Cp, gx=D, gt=E, N=1, C=8, H=16, W=16, K=3, dt=F32):
+    return lib.ddpm_filter_bwd(x, taps, g, gx, gt, N, C, H, W, K, dt, None)
+
+
 def _fused(lib, x=A, y=B, w=Cp, b=D, out=E, N=1, C=8, H=16, W=16, K=3, dt=F32):
     return lib.ddpm_fused_fwd(x, y, w, b, out, N, C, H, W, K, dt, None)
 
@@ -80,7 +85,7 @@ def _reduce(lib, pw=A, pb=B, S=1, gw=Cp, gb=D, C=8, K=3, dt=F32):
     return lib.ddpm_reduce_partials(pw, pb, S, gw, gb, C, K, dt, None)
 
 
-@pytest.mark.parametrize("call", [_filter, _fused, _bwd])
+@pytest.mark.parametrize("call", [_filter, _filter_bwd, _fused, _bwd])
 def test_shape_validation(lib, call):
     for kw in (dict(N=0), dict(C=0), dict(H=0), dict(W=-1), dict(C=4096), dict(dt=2), dict(dt=-1),
                dict(H=1 << 16, W=1 << 15)):
@@ -102,6 +107,10 @@ def test_null_and_misaligned_pointers(lib):
     assert _bwd(lib, pw=Hp + 2, dt=BF16) == INVALID      # partials are float32 in every dtype
     for name in ("pw", "pb", "gw", "gb"):
         assert _reduce(lib, **{name: 0}) == INVALID
+    for name in ("x", "taps", "g"):
+        assert _filter_bwd(lib, **{name: 0}) == INVALID
+    assert _filter_bwd(lib, gx=0, gt=0) == INVALID        # nothing requested
+    assert _filter_bwd(lib, gt=B) == INVALID              # grad_taps overlaps taps
 
 
 def test_partial_count_validation(lib):

@@ -19,7 +19,8 @@ import torch
 
 import dynamic_dilated_depthwise_amd as ddpm
 from dynamic_dilated_depthwise_amd import synth
-from gpu_cases import (TOL, announce, assert_close, dev, f64, gpu_bwd, gpu_filter, gpu_fused, inputs, orc)
+from gpu_cases import (TOL, announce, assert_close, dev, f64, gpu_bwd, gpu_filter, gpu_filter_bwd, gpu_fused, inputs,
+                       orc)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +114,51 @@ def test_fused_bwd(name, spec, dt):
         assert_close(f64(got), ref, tol, f"{what} {name} {dt}")
 
 
+def _check_filter_bwd(gx, gk, ref, dtype, what):
+    rdx, rdk = ref
+    if gk is not None:
+        exact = torch.from_numpy(rdk).to(dtype)
+        bad = (gk.cpu() != exact)
+        assert not bool(bad.any()), f"{what}: dtaps differs from the rounded exact product at " \
+            f"{int(bad.sum())} elements"
+    if gx is not None:
+        assert_close(f64(gx), rdx, TOL[dtype]["grad"], f"{what} dx")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name,spec", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_filter_bwd(name, spec, dt):
+    shape, block = _resolve(name, spec)
+    dtype = DT[dt]
+    h = inputs(shape, block, dtype, taps=True, grad=True)
+    a = {k: f64(v) for k, v in h.items()}
+    ref = orc().filter_bwd(a["x"], a["taps"], a["grad_out"], shape.K)
+    announce("filter_bwd", name, dt, shape)
+    gx, gk = gpu_filter_bwd(dev(h), shape.K)
+    _check_filter_bwd(gx, gk, ref, dtype, f"filter_bwd {name} {dt}")
+
+
+FILTER_BWD_ONE_OUTPUT = ["nonaligned", "nonaligned_k5", "ragged_tiles", "one_row_k5", "c2_k5_tall", "c64_w200_k5"]
+
+
+@pytest.mark.parametrize("want", ["dx", "dk"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name", FILTER_BWD_ONE_OUTPUT)
+def test_filter_bwd_one_output(name, dt, want):
+    """Requesting one gradient runs a separate kernel instance; it must give the
+    same values as the oracle (and hence as the instance computing both)."""
+    spec = dict(FWD_CASES)[name]
+    shape, block = _resolve(name, spec)
+    dtype = DT[dt]
+    h = inputs(shape, block, dtype, taps=True, grad=True)
+    a = {k: f64(v) for k, v in h.items()}
+    ref = orc().filter_bwd(a["x"], a["taps"], a["grad_out"], shape.K)
+    announce("filter_bwd", want, name, dt, shape)
+    gx, gk = gpu_filter_bwd(dev(h), shape.K, want_dx=want == "dx", want_dk=want == "dk")
+    assert (gx is None) == (want != "dx") and (gk is None) == (want != "dk")
+    _check_filter_bwd(gx, gk, ref, dtype, f"filter_bwd[{want}] {name} {dt}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_misaligned_pointers(dt):
     """Element-aligned (not 16-byte aligned) tensors take the scalar/unaligned paths."""
@@ -139,6 +185,8 @@ def test_misaligned_pointers(dt):
     got = gpu_bwd(d, K)[:4]
     for what, g_, r_ in zip(("dx", "dy", "dweight", "dbias"), got, refs):
         assert_close(f64(g_), r_, TOL[dtype]["grad"], what)
+    gx, gk = gpu_filter_bwd(d, K)
+    _check_filter_bwd(gx, gk, o.filter_bwd(a["x"], a["taps"], a["grad_out"], K), dtype, "filter_bwd")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -166,8 +214,8 @@ def test_bitwise_deterministic(name):
     shape, block = synth.WORKLOADS[name]
     d = dev(inputs(shape, block, torch.float32, grad=True, taps=True))
     announce("determinism", name)
-    r1 = (gpu_filter(d, shape.K), gpu_fused(d, shape.K), *gpu_bwd(d, shape.K))
-    r2 = (gpu_filter(d, shape.K), gpu_fused(d, shape.K), *gpu_bwd(d, shape.K))
+    r1 = (gpu_filter(d, shape.K), gpu_fused(d, shape.K), *gpu_bwd(d, shape.K), *gpu_filter_bwd(d, shape.K))
+    r2 = (gpu_filter(d, shape.K), gpu_fused(d, shape.K), *gpu_bwd(d, shape.K), *gpu_filter_bwd(d, shape.K))
     for u, v in zip(r1, r2):
         assert torch.equal(u, v)
 
