@@ -10,10 +10,11 @@
 //
 // Like the forward filter this is an HBM stream (3K^2 tap planes read for dX, 3K^2
 // dK planes written).  One workgroup = one (n, c) plane x a TH x TW tile in
-// XCD-contiguous order; x and / or the three G_b planes of the tile plus a
-// 5*(K-1)/2 halo are staged once in LDS (zero outside the image), so the dilated
-// neighbourhoods come from LDS; each thread owns VEC consecutive pixels of a row.
-// The dK planes are streamed out with non-temporal vector stores.
+// XCD-contiguous order, and each thread owns VEC consecutive pixels of a row.  The
+// dilated neighbourhoods come from LDS (float, zero outside the image): x with the
+// full 5*(K-1)/2 halo for dK, and for dX one G_b plane per dilation, staged with
+// only that dilation's D*(K-1)/2 halo, so two planes of LDS serve all three.  The
+// dK planes are streamed out with non-temporal vector stores.
 #include "common.hpp"
 #include "launchers.hpp"
 
@@ -42,7 +43,7 @@ template <typename T, int K, int VEC, bool WANT_DX, bool WANT_DK>
 __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x, const T *__restrict__ taps,
                                                          const T *__restrict__ gout, T *__restrict__ gx,
                                                          T *__restrict__ gtaps, int C, int H, int W, int TH, int TW,
-                                                         int nbands, int ncolt, int aligned) {
+                                                         int nbands, int ncolt, int aligned, int vec_stage) {
     constexpr int r = (K - 1) / 2;
     constexpr int HALO = 5 * r;
     constexpr int PADC = (HALO + 3) & ~3;
@@ -63,79 +64,68 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
     const int w0 = colt * TW;
     const int64_t HW = (int64_t)H * W;
     const T *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
+    const bool vst = vec_stage != 0;
 
-    // Staged planes: [0] x (for dK), [1 + b] G_b (for dX).
+    // LDS: x with the full halo (dK), then one G_b plane at a time (dX).
     float *xs = lds;
     float *gs = lds + (WANT_DK ? LP : 0);
-    for (int i = threadIdx.x; i < LP; i += blockDim.x) {
-        const int lr = i / LW;
-        const int lc = i - lr * LW;
-        const int hh = h0 - HALO + lr;
-        const int ww = w0 - PADC + lc;
-        const bool in = hh >= 0 && hh < H && ww >= 0 && ww < W;
-        const int64_t pix = (int64_t)hh * W + ww;
-        if constexpr (WANT_DK) xs[i] = in ? Elem<T>::to_f32(x[(int64_t)nc * HW + pix]) : 0.f;
-        if constexpr (WANT_DX) {
-#pragma unroll
-            for (int b = 0; b < 3; ++b)
-                gs[b * LP + i] = in ? Elem<T>::to_f32(gn[(int64_t)((1 + b) * C + c) * HW + pix]) : 0.f;
-        }
-    }
-    __syncthreads();
+    if constexpr (WANT_DK) stage_rows<T>(x + (int64_t)nc * HW, h0, w0, H, W, HALO, PADC, LW, 0, LH, xs, vst);
 
+    // TH * TW / VEC == 256: each thread owns one run of VEC pixels of one row.
+    const int gpr = TW / VEC;
+    const int lr = threadIdx.x / gpr;
+    const int lc = (threadIdx.x - lr * gpr) * VEC;
+    const int h = h0 + lr;
+    const int w = w0 + lc;
+    const bool active = h < H && w < W;  // W % VEC == 0: a run is wholly in or out
+    const int64_t pix = (int64_t)h * W + w;
+    const int ctr = (lr + HALO) * LW + lc + PADC;  // staged index of the run's first pixel
     const int64_t R = 3LL * C * KK;
     const T *__restrict__ tp = taps + (int64_t)n * R * HW;
     T *__restrict__ dkp = gtaps + (int64_t)n * R * HW;
-    const int gpr = TW / VEC;
-    for (int gi = threadIdx.x; gi < TH * gpr; gi += blockDim.x) {
-        const int lr = gi / gpr;
-        const int lc = (gi - lr * gpr) * VEC;
-        const int h = h0 + lr;
-        const int w = w0 + lc;
-        if (h >= H || w >= W) continue;  // W % VEC == 0: a vector is wholly in or out
-        const int64_t pix = (int64_t)h * W + w;
-        const int ctr = (lr + HALO) * LW + lc + PADC;  // staged index of this run's first pixel
+
+    float acc[VEC];
+    if constexpr (WANT_DX) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] = active ? Elem<T>::to_f32(gn[(int64_t)c * HW + pix + k]) : 0.f;
+    }
+
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+        const int D = dilation(b);
+        const T *__restrict__ gbp = gn + (int64_t)((1 + b) * C + c) * HW;
+        if constexpr (WANT_DX) {
+            // G_b is read only D*r rows and columns beyond the tile.
+            if (b > 0) __syncthreads();  // every thread is done with G_{b-1}
+            stage_rows<T>(gbp, h0, w0, H, W, HALO, PADC, LW, HALO - D * r, HALO + TH + D * r, gs, vst);
+        }
+        if (b == 0 || WANT_DX) __syncthreads();
+        if (!active) continue;
 
         if constexpr (WANT_DK) {
+            float gv[VEC];
 #pragma unroll
-            for (int b = 0; b < 3; ++b) {
-                const int D = dilation(b);
-                float gv[VEC];
-                if constexpr (WANT_DX) {
+            for (int k = 0; k < VEC; ++k) gv[k] = WANT_DX ? gs[ctr + k] : Elem<T>::to_f32(gbp[pix + k]);
 #pragma unroll
-                    for (int k = 0; k < VEC; ++k) gv[k] = gs[b * LP + ctr + k];
-                } else {
-                    const T *gb = gn + (int64_t)((1 + b) * C + c) * HW + pix;
+            for (int t = 0; t < KK; ++t) {
+                const int ki = t / K, kj = t % K;
+                const float *xn = xs + ctr + (ki - r) * D * LW + (kj - r) * D;
+                V dv;
 #pragma unroll
-                    for (int k = 0; k < VEC; ++k) gv[k] = Elem<T>::to_f32(gb[k]);
-                }
-#pragma unroll
-                for (int t = 0; t < KK; ++t) {
-                    const int ki = t / K, kj = t % K;
-                    const float *xn = xs + ctr + (ki - r) * D * LW + (kj - r) * D;
-                    V dv;
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) set_lane<V, T, VEC>(dv, k, Elem<T>::from_f32(gv[k] * xn[k]));
-                    const int64_t plane = (int64_t)(b * C + c) * KK + t;
-                    __builtin_nontemporal_store(dv, (V *)(dkp + plane * HW + pix));
-                }
+                for (int k = 0; k < VEC; ++k) set_lane<V, T, VEC>(dv, k, Elem<T>::from_f32(gv[k] * xn[k]));
+                const int64_t plane = (int64_t)(b * C + c) * KK + t;
+                __builtin_nontemporal_store(dv, (V *)(dkp + plane * HW + pix));
             }
         }
         if constexpr (WANT_DX) {
-            float acc[VEC];
-            const T *gxs = gn + (int64_t)c * HW + pix;
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) acc[k] = Elem<T>::to_f32(gxs[k]);
-            // One dilation (K <= 3, VEC <= 4) or one kernel row at a time: the shifted tap
-            // runs of a chunk are issued together without holding all 3K^2 in registers.
+            // The source runs of one kernel row (K = 5, or 8-wide runs) or of the whole
+            // dilation are issued together, without holding all 3K^2 in registers.
             constexpr int CH = (K <= 3 && VEC <= 4) ? KK : K;
 #pragma unroll 1
-            for (int bt = 0; bt < 3 * KK; bt += CH) {
-                const int b = bt / KK;
-                const int D = dilation(b);
+            for (int t0 = 0; t0 < KK; t0 += CH) {
 #pragma unroll
                 for (int j = 0; j < CH; ++j) {
-                    const int t = bt - b * KK + j;
+                    const int t = t0 + j;
                     const int ki = t / K, kj = t % K;
                     const int dr = (ki - r) * D, dc = (kj - r) * D;
                     const int hs = h - dr;
@@ -144,11 +134,15 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
                     float tv[VEC];
                     load_run<T, VEC>(tp + plane * HW + (int64_t)(hok ? hs : 0) * W, w - dc, W, hok, aligned != 0,
                                      tv);
-                    const float *gsn = gs + b * LP + ctr - dr * LW - dc;
+                    const float *gsn = gs + ctr - dr * LW - dc;
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) acc[k] += tv[k] * gsn[k];
                 }
             }
+        }
+    }
+    if constexpr (WANT_DX) {
+        if (active) {
             V ov;
 #pragma unroll
             for (int k = 0; k < VEC; ++k) set_lane<V, T, VEC>(ov, k, Elem<T>::from_f32(acc[k]));
@@ -160,8 +154,8 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
 template <typename T, int K, int VEC, bool DX, bool DK>
 static hipError_t launch_filter_bwd_t(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N,
                                       int C, int H, int W, bool al, hipStream_t stream) {
-    // dK alone stages one plane: wide rows as in the forward filter.  dX stages three
-    // G_b planes: narrower, taller tiles keep the halo share and the LDS per block down.
+    // dK alone: wide rows as in the forward filter.  dX re-stages G_b per dilation:
+    // narrower, taller tiles keep the halo share down.
     const int max_tpr = DX ? 32 : 64;
     int tw = VEC;
     while (tw < W && tw < max_tpr * VEC) tw *= 2;
@@ -169,7 +163,7 @@ static hipError_t launch_filter_bwd_t(const void *x, const void *taps, const voi
     const int TH = 256 / (TW / VEC) > 0 ? 256 / (TW / VEC) : 1;
     constexpr int HALO = 5 * ((K - 1) / 2);
     constexpr int PADC = (HALO + 3) & ~3;
-    const size_t planes = (DK ? 1 : 0) + (DX ? 3 : 0);
+    const size_t planes = (DK ? 1 : 0) + (DX ? 1 : 0);
     const size_t lds = sizeof(float) * planes * (size_t)(TH + 2 * HALO) * (TW + 2 * PADC);
     auto kern = filter_bwd_kernel<T, K, VEC, DX, DK>;
     if (lds > 64 * 1024) {
@@ -180,8 +174,10 @@ static hipError_t launch_filter_bwd_t(const void *x, const void *taps, const voi
     const int ncolt = (W + TW - 1) / TW;
     const int64_t nblk = (int64_t)N * C * nbands * ncolt;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const uintptr_t pal = Elem<T>::is_bf16 ? 8 : 16;
+    const int vec_stage = (W % 4 == 0) && ((uintptr_t)x % pal == 0) && ((uintptr_t)gout % pal == 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), lds, stream, (const T *)x, (const T *)taps,
-                       (const T *)gout, (T *)gx, (T *)gtaps, C, H, W, TH, TW, nbands, ncolt, al ? 1 : 0);
+                       (const T *)gout, (T *)gx, (T *)gtaps, C, H, W, TH, TW, nbands, ncolt, al ? 1 : 0, vec_stage);
     return hipGetLastError();
 }
 

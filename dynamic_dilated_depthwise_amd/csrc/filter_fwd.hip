@@ -41,29 +41,9 @@ __global__ __launch_bounds__(256) void filter_fwd_kernel(const T *__restrict__ x
     const int w0 = colt * TW;
     const int64_t HW = (int64_t)H * W;
 
-    // Stage rows h0-HALO .. h0+TH+HALO-1, columns w0-PADC .. w0+TW+PADC-1 of x.
-    const T *__restrict__ xp = x + (int64_t)nc * HW;
-    if (vec_stage) {  // W % 4 == 0 and x 16-byte (float) / 8-byte (bf16) aligned
-        const int nv = LH * (LW / 4);
-        for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-            const int lr = i / (LW / 4);
-            const int cv = i - lr * (LW / 4);
-            const int hh = h0 - HALO + lr;
-            const int ww = w0 - PADC + 4 * cv;
-            const f32x4 v = load4_row(xp + (int64_t)(hh >= 0 && hh < H ? hh : 0) * W, ww, W, hh >= 0 && hh < H, true);
-            *(f32x4 *)(xs + lr * LW + 4 * cv) = v;
-        }
-    } else {
-        for (int i = threadIdx.x; i < LH * LW; i += blockDim.x) {
-            const int lr = i / LW;
-            const int lc = i - lr * LW;
-            const int hh = h0 - HALO + lr;
-            const int ww = w0 - PADC + lc;
-            float v = 0.f;
-            if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = Elem<T>::to_f32(xp[(int64_t)hh * W + ww]);
-            xs[i] = v;
-        }
-    }
+    // Stage rows h0-HALO .. h0+TH+HALO-1, columns w0-PADC .. w0+TW+PADC-1 of x
+    // (vec_stage: W % 4 == 0 and x 16-byte (float) / 8-byte (bf16) aligned).
+    stage_rows<T>(x + (int64_t)nc * HW, h0, w0, H, W, HALO, PADC, LW, 0, LH, xs, vec_stage != 0);
     __syncthreads();
 
     const int64_t R = 3LL * C * KK;
