@@ -39,7 +39,23 @@ __device__ __forceinline__ void load_run(const T *__restrict__ row, int w, int W
     }
 }
 
-template <typename T, int K, int VEC, bool WANT_DX, bool WANT_DK>
+// The value v holds in the lane `off` places away in this wave (lane l reads lane
+// l + off), through whole-wave DPP shifts: wave_shr:1 moves lane l-1 into lane l,
+// wave_shl:1 lane l+1.  Lanes past either end of the wave read 0.  `off` is a
+// compile-time constant wherever this is inlined, so the loops fold away.
+__device__ __forceinline__ float lane_from(float v, int off) {
+    for (; off < 0; ++off) v = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, true));
+    for (; off > 0; --off) v = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true));
+    return v;
+}
+
+constexpr int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// LS (lane shift): one tile spans the whole image row, so the VEC-pixel runs of a row
+// sit in consecutive lanes of one wave.  dX then reads every tap run at its own
+// aligned position of the shifted row and takes the column offset from neighbouring
+// lanes; otherwise each run is loaded at the shifted column with bounds checks.
+template <typename T, int K, int VEC, bool WANT_DX, bool WANT_DK, bool LS>
 __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x, const T *__restrict__ taps,
                                                          const T *__restrict__ gout, T *__restrict__ gx,
                                                          T *__restrict__ gtaps, int C, int H, int W, int TH, int TW,
@@ -100,9 +116,8 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
             stage_rows<T>(gbp, h0, w0, H, W, HALO, PADC, LW, HALO - D * r, HALO + TH + D * r, gs, vst);
         }
         if (b == 0 || WANT_DX) __syncthreads();
-        if (!active) continue;
 
-        if constexpr (WANT_DK) {
+        if (WANT_DK && active) {
             float gv[VEC];
 #pragma unroll
             for (int k = 0; k < VEC; ++k) gv[k] = WANT_DX ? gs[ctr + k] : Elem<T>::to_f32(gbp[pix + k]);
@@ -117,7 +132,43 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
                 __builtin_nontemporal_store(dv, (V *)(dkp + plane * HW + pix));
             }
         }
-        if constexpr (WANT_DX) {
+        if constexpr (WANT_DX && LS) {
+            // Every lane of the wave takes part (the shifts read neighbouring lanes);
+            // lanes past the image hold zeros.  A value moved in from lane l + m counts
+            // only if that lane's run starts inside this image row.
+            constexpr int LM = (HALO + VEC - 1) / VEC + 1;
+            bool src_ok[2 * LM + 1];
+#pragma unroll
+            for (int m = -LM; m <= LM; ++m) src_ok[m + LM] = (unsigned)(w + m * VEC) < (unsigned)W;
+            // One kernel row (K runs in flight) per iteration keeps registers low.
+#pragma unroll 1
+            for (int ki = 0; ki < K; ++ki) {
+                const int dr = (ki - r) * D;
+                const int hs = h - dr;
+                const bool hok = active && hs >= 0 && hs < H;
+                const int64_t row = (int64_t)((b * C + c) * KK + ki * K) * HW + (int64_t)(hok ? hs : 0) * W + w;
+                const float *grow = gs + ctr - dr * LW;
+#pragma unroll
+                for (int kj = 0; kj < K; ++kj) {
+                    const int dc = (kj - r) * D;
+                    V rv = {};
+                    if (hok) rv = __builtin_nontemporal_load((const V *)(tp + row + (int64_t)kj * HW));
+                    float raw[VEC];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) raw[e] = Elem<T>::to_f32(lane_of<V, T, VEC>(rv, e));
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) {
+                        const int src = j - dc;  // column of the source pixel, relative to w
+                        const int m = floor_div(src, VEC);
+                        float v = lane_from(raw[src - m * VEC], m);
+                        if (m != 0) v = src_ok[m + LM] ? v : 0.f;
+                        acc[j] += v * grow[j - dc];
+                    }
+                }
+            }
+        }
+        if constexpr (WANT_DX && !LS) {
+            if (!active) continue;
             // The source runs of one kernel row (K = 5, or 8-wide runs) or of the whole
             // dilation are issued together, without holding all 3K^2 in registers.
             constexpr int CH = (K <= 3 && VEC <= 4) ? KK : K;
@@ -151,21 +202,23 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
     }
 }
 
-template <typename T, int K, int VEC, bool DX, bool DK>
+template <typename T, int K, int VEC, bool DX, bool DK, bool LS>
 static hipError_t launch_filter_bwd_t(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N,
                                       int C, int H, int W, bool al, hipStream_t stream) {
-    // dK alone: wide rows as in the forward filter.  dX re-stages G_b per dilation:
-    // narrower, taller tiles keep the halo share down.
-    const int max_tpr = DX ? 32 : 64;
+    // dK alone and the lane-shift dX: wide rows (a tile spans the row when it fits in
+    // 64 runs).  The checked dX re-stages G_b per dilation: narrower, taller tiles
+    // keep the halo share down.
+    const int max_tpr = (DX && !LS) ? 32 : 64;
     int tw = VEC;
     while (tw < W && tw < max_tpr * VEC) tw *= 2;
     const int TW = tw;
+    if (LS && TW < W) return hipErrorInvalidValue;
     const int TH = 256 / (TW / VEC) > 0 ? 256 / (TW / VEC) : 1;
     constexpr int HALO = 5 * ((K - 1) / 2);
     constexpr int PADC = (HALO + 3) & ~3;
     const size_t planes = (DK ? 1 : 0) + (DX ? 1 : 0);
     const size_t lds = sizeof(float) * planes * (size_t)(TH + 2 * HALO) * (TW + 2 * PADC);
-    auto kern = filter_bwd_kernel<T, K, VEC, DX, DK>;
+    auto kern = filter_bwd_kernel<T, K, VEC, DX, DK, LS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -184,11 +237,16 @@ static hipError_t launch_filter_bwd_t(const void *x, const void *taps, const voi
 template <typename T, int K, int VEC>
 static hipError_t launch_filter_bwd_v(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N,
                                       int C, int H, int W, bool al, hipStream_t stream) {
-    if (gx != nullptr && gtaps != nullptr)
-        return launch_filter_bwd_t<T, K, VEC, true, true>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
-    if (gx != nullptr)
-        return launch_filter_bwd_t<T, K, VEC, true, false>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
-    return launch_filter_bwd_t<T, K, VEC, false, true>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
+    if (gx == nullptr)
+        return launch_filter_bwd_t<T, K, VEC, false, true, false>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
+    // Lane shifts need the row in one tile and vector-aligned tap runs.
+    const bool ls = W <= 64 * VEC && (uintptr_t)taps % (VEC * sizeof(T)) == 0;
+    if (gtaps != nullptr) {
+        if (ls) return launch_filter_bwd_t<T, K, VEC, true, true, true>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
+        return launch_filter_bwd_t<T, K, VEC, true, true, false>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
+    }
+    if (ls) return launch_filter_bwd_t<T, K, VEC, true, false, true>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
+    return launch_filter_bwd_t<T, K, VEC, true, false, false>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
 }
 
 template <typename T, int K>

@@ -37,6 +37,8 @@ FWD_CASES = [
     ("c33", (S_(1, 33, 10, 8, 3), 109)), ("c70_streamed", (S_(1, 70, 12, 20, 3), 110)),
     ("c1024_max", (S_(1, 1024, 2, 2, 3), 111)), ("c2_k5_tall", (S_(2, 2, 37, 6, 5), 112)),
     ("c48_ragged", (S_(1, 48, 12, 70, 3), 113)), ("c64_w200_k5", (S_(1, 64, 9, 200, 5), 114)),
+    # rows wider than one tile (several column tiles; the checked backward dX path)
+    ("w520_wide", (S_(1, 4, 6, 520, 3), 115)), ("w1030_k5", (S_(1, 3, 5, 1030, 5), 116)),
 ]
 
 BWD_CASES = [
@@ -138,7 +140,8 @@ def test_filter_bwd(name, spec, dt):
     _check_filter_bwd(gx, gk, ref, dtype, f"filter_bwd {name} {dt}")
 
 
-FILTER_BWD_ONE_OUTPUT = ["nonaligned", "nonaligned_k5", "ragged_tiles", "one_row_k5", "c2_k5_tall", "c64_w200_k5"]
+FILTER_BWD_ONE_OUTPUT = ["nonaligned", "nonaligned_k5", "ragged_tiles", "one_row_k5", "c2_k5_tall", "c64_w200_k5",
+                         "w520_wide"]
 
 
 @pytest.mark.parametrize("want", ["dx", "dk"])
