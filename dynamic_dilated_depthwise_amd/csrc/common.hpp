@@ -118,40 +118,6 @@ __device__ __forceinline__ f32x4 load4_row(const T *__restrict__ row, int w, int
     return v;
 }
 
-// Stage LDS rows [lr0, lr1) of a tile of one image plane as float: LDS row lr,
-// column lc holds pixel (h0 - HALO + lr, w0 - PADC + lc), zero outside the image.
-// Rows are LW floats.  vec: four pixels per load, which needs W % 4 == 0, LW and
-// w0 - PADC multiples of 4, and a plane base aligned to four elements.
-template <typename T>
-__device__ __forceinline__ void stage_rows(const T *__restrict__ p, int h0, int w0, int H, int W, int HALO, int PADC,
-                                           int LW, int lr0, int lr1, float *__restrict__ dst, bool vec) {
-    if (vec) {
-        const int vpr = LW >> 2;
-        const int nv = (lr1 - lr0) * vpr;
-        for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-            const int q = i / vpr;
-            const int cv = i - q * vpr;
-            const int lr = lr0 + q;
-            const int hh = h0 - HALO + lr;
-            const bool ok = hh >= 0 && hh < H;
-            const f32x4 v = load4_row(p + (int64_t)(ok ? hh : 0) * W, w0 - PADC + 4 * cv, W, ok, true);
-            *(f32x4 *)(dst + lr * LW + 4 * cv) = v;
-        }
-    } else {
-        const int n = (lr1 - lr0) * LW;
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const int q = i / LW;
-            const int lc = i - q * LW;
-            const int lr = lr0 + q;
-            const int hh = h0 - HALO + lr;
-            const int ww = w0 - PADC + lc;
-            float v = 0.f;
-            if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = Elem<T>::to_f32(p[(int64_t)hh * W + ww]);
-            dst[lr * LW + lc] = v;
-        }
-    }
-}
-
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 // Four consecutive pixels w..w+3 of a row with no bounds checks, for the case the
@@ -315,6 +281,52 @@ template <typename T> __device__ __forceinline__ T exact_narrow(float v);
 template <> __device__ __forceinline__ float exact_narrow<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t exact_narrow<bf16_t>(float v) {
     return (bf16_t)(__float_as_uint(v) >> 16);
+}
+
+// Stage LDS rows [lr0, lr1) of a tile of one image plane: LDS row lr, column lc
+// holds pixel (h0 - HALO + lr, w0 - PADC + lc), zero outside the image, as float
+// (D = float) or as the input's own bits (D = T).  Rows are LW elements.  vec: four
+// pixels per load, which needs W % 4 == 0, LW and w0 - PADC multiples of 4, and a
+// plane base aligned to four elements.
+template <typename D, typename T> __device__ __forceinline__ D lds_elem(float v) {
+    if constexpr (sizeof(D) == sizeof(float)) return v;
+    else return exact_narrow<T>(v);
+}
+template <typename T, typename D = float>
+__device__ __forceinline__ void stage_rows(const T *__restrict__ p, int h0, int w0, int H, int W, int HALO, int PADC,
+                                           int LW, int lr0, int lr1, D *__restrict__ dst, bool vec) {
+    if (vec) {
+        const int vpr = LW >> 2;
+        const int nv = (lr1 - lr0) * vpr;
+        for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+            const int q = i / vpr;
+            const int cv = i - q * vpr;
+            const int lr = lr0 + q;
+            const int hh = h0 - HALO + lr;
+            const bool ok = hh >= 0 && hh < H;
+            const f32x4 v = load4_row(p + (int64_t)(ok ? hh : 0) * W, w0 - PADC + 4 * cv, W, ok, true);
+            if constexpr (sizeof(D) == sizeof(float)) {
+                *(f32x4 *)(dst + lr * LW + 4 * cv) = v;
+            } else {
+                u16x4 u;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) u[k] = exact_narrow<T>(v[k]);
+                *(u16x4 *)(dst + lr * LW + 4 * cv) = u;
+            }
+        }
+    } else {
+        const int n = (lr1 - lr0) * LW;
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int q = i / LW;
+            const int lc = i - q * LW;
+            const int lr = lr0 + q;
+            const int hh = h0 - HALO + lr;
+            const int ww = w0 - PADC + lc;
+            float v = 0.f;
+            if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = Elem<T>::to_f32(p[(int64_t)hh * W + ww]);
+            dst[lr * LW + lc] = lds_elem<D, T>(v);
+        }
+    }
 }
 
 // Raw (bit-exact) copy helpers for the x block of the output.

@@ -52,9 +52,10 @@ __device__ __forceinline__ float lane_from(float v, int off) {
 constexpr int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
 // LS (lane shift): one tile spans the whole image row, so the VEC-pixel runs of a row
-// sit in consecutive lanes of one wave.  dX then reads every tap run at its own
-// aligned position of the shifted row and takes the column offset from neighbouring
-// lanes; otherwise each run is loaded at the shifted column with bounds checks.
+// sit in consecutive lanes of one wave.  Every operand is then read at the lane's own
+// aligned position of the shifted row and the column offset is taken from
+// neighbouring lanes; otherwise shifted runs are read from LDS at the offset column
+// and tap runs are loaded at the shifted column with bounds checks.
 template <typename T, int K, int VEC, bool WANT_DX, bool WANT_DK, bool LS>
 __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x, const T *__restrict__ taps,
                                                          const T *__restrict__ gout, T *__restrict__ gx,
@@ -62,10 +63,13 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
                                                          int nbands, int ncolt, int aligned, int vec_stage) {
     constexpr int r = (K - 1) / 2;
     constexpr int HALO = 5 * r;
-    constexpr int PADC = (HALO + 3) & ~3;
+    constexpr int PADC = LS ? 0 : (HALO + 3) & ~3;  // lane shifts never read beyond the tile's columns
     constexpr int KK = K * K;
     typedef typename VecOf<T, VEC>::type V;
-    extern __shared__ float lds[];
+    // Lane shifts read LDS only at the lane's own aligned runs: the input's own bits
+    // are staged (half the LDS for bfloat16); the checked path reads shifted floats.
+    typedef typename std::conditional<LS, T, float>::type LT;
+    extern __shared__ __align__(16) unsigned char lds_bytes[];
 
     const int LW = TW + 2 * PADC;
     const int LH = TH + 2 * HALO;
@@ -83,8 +87,8 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
     const bool vst = vec_stage != 0;
 
     // LDS: x with the full halo (dK), then one G_b plane at a time (dX).
-    float *xs = lds;
-    float *gs = lds + (WANT_DK ? LP : 0);
+    LT *xs = (LT *)lds_bytes;
+    LT *gs = xs + (WANT_DK ? LP : 0);
     if constexpr (WANT_DK) stage_rows<T>(x + (int64_t)nc * HW, h0, w0, H, W, HALO, PADC, LW, 0, LH, xs, vst);
 
     // TH * TW / VEC == 256: each thread owns one run of VEC pixels of one row.
@@ -117,77 +121,122 @@ __global__ __launch_bounds__(256) void filter_bwd_kernel(const T *__restrict__ x
         }
         if (b == 0 || WANT_DX) __syncthreads();
 
-        if (WANT_DK && active) {
-            float gv[VEC];
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) gv[k] = WANT_DX ? gs[ctr + k] : Elem<T>::to_f32(gbp[pix + k]);
-#pragma unroll
-            for (int t = 0; t < KK; ++t) {
-                const int ki = t / K, kj = t % K;
-                const float *xn = xs + ctr + (ki - r) * D * LW + (kj - r) * D;
-                V dv;
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) set_lane<V, T, VEC>(dv, k, Elem<T>::from_f32(gv[k] * xn[k]));
-                const int64_t plane = (int64_t)(b * C + c) * KK + t;
-                __builtin_nontemporal_store(dv, (V *)(dkp + plane * HW + pix));
-            }
-        }
-        if constexpr (WANT_DX && LS) {
-            // Every lane of the wave takes part (the shifts read neighbouring lanes);
-            // lanes past the image hold zeros.  A value moved in from lane l + m counts
-            // only if that lane's run starts inside this image row.
+        if constexpr (LS) {
+            // Per kernel row: one aligned row of x (dK) and of G_b (dX) from LDS serves
+            // all K taps; the column offset is taken from neighbouring lanes.  Every
+            // lane of the wave takes part; lanes past the image hold zeros or are
+            // masked.  A value moved in from lane l + m counts only if that lane's run
+            // starts inside this image row.
             constexpr int LM = (HALO + VEC - 1) / VEC + 1;
             bool src_ok[2 * LM + 1];
 #pragma unroll
             for (int m = -LM; m <= LM; ++m) src_ok[m + LM] = (unsigned)(w + m * VEC) < (unsigned)W;
-            // One kernel row (K runs in flight) per iteration keeps registers low.
+            // Runs start at multiples of VEC elements of LDS (LW = TW, lc and the plane
+            // size are multiples of VEC), so they are read as aligned vectors.
+            auto lds_run = [](const LT *p, float(&v)[VEC]) {
+                const V u = *(const V *)p;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) v[k] = Elem<T>::to_f32(lane_of<V, T, VEC>(u, k));
+            };
+            float gv[VEC];  // G_b at the lane's own pixels (dK)
+            if constexpr (WANT_DK) {
+                if constexpr (WANT_DX) {
+                    lds_run(gs + ctr, gv);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) gv[k] = active ? Elem<T>::to_f32(gbp[pix + k]) : 0.f;
+                }
+            }
 #pragma unroll 1
             for (int ki = 0; ki < K; ++ki) {
                 const int dr = (ki - r) * D;
-                const int hs = h - dr;
-                const bool hok = active && hs >= 0 && hs < H;
-                const int64_t row = (int64_t)((b * C + c) * KK + ki * K) * HW + (int64_t)(hok ? hs : 0) * W + w;
-                const float *grow = gs + ctr - dr * LW;
+                if constexpr (WANT_DK) {
+                    // dK[p] = G_b[p] * x[p + (dr, dc)]
+                    float xr[VEC];
+                    lds_run(xs + ctr + dr * LW, xr);
 #pragma unroll
-                for (int kj = 0; kj < K; ++kj) {
-                    const int dc = (kj - r) * D;
-                    V rv = {};
-                    if (hok) rv = __builtin_nontemporal_load((const V *)(tp + row + (int64_t)kj * HW));
-                    float raw[VEC];
+                    for (int kj = 0; kj < K; ++kj) {
+                        const int dc = (kj - r) * D;
+                        V dv;
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) raw[e] = Elem<T>::to_f32(lane_of<V, T, VEC>(rv, e));
+                        for (int e = 0; e < VEC; ++e) {
+                            const int src = e + dc;
+                            const int m = floor_div(src, VEC);
+                            float xv = lane_from(xr[src - m * VEC], m);
+                            if (m != 0) xv = src_ok[m + LM] ? xv : 0.f;
+                            set_lane<V, T, VEC>(dv, e, Elem<T>::from_f32(gv[e] * xv));
+                        }
+                        const int64_t plane = (int64_t)(b * C + c) * KK + ki * K + kj;
+                        if (active) __builtin_nontemporal_store(dv, (V *)(dkp + plane * HW + pix));
+                    }
+                }
+                if constexpr (WANT_DX) {
+                    // dX[q] += taps[q - (dr, dc)] * G_b[q - (dr, dc)]: the product is formed
+                    // at the source pixel (the lane's own aligned run of row h - dr) and
+                    // then moved by dc columns.
+                    const int hs = h - dr;
+                    const bool hok = active && hs >= 0 && hs < H;
+                    const int64_t row =
+                        (int64_t)((b * C + c) * KK + ki * K) * HW + (int64_t)(hok ? hs : 0) * W + w;
+                    float gr[VEC];
+                    lds_run(gs + ctr - dr * LW, gr);
 #pragma unroll
-                    for (int j = 0; j < VEC; ++j) {
-                        const int src = j - dc;  // column of the source pixel, relative to w
-                        const int m = floor_div(src, VEC);
-                        float v = lane_from(raw[src - m * VEC], m);
-                        if (m != 0) v = src_ok[m + LM] ? v : 0.f;
-                        acc[j] += v * grow[j - dc];
+                    for (int kj = 0; kj < K; ++kj) {
+                        const int dc = (kj - r) * D;
+                        V rv = {};
+                        if (hok) rv = __builtin_nontemporal_load((const V *)(tp + row + (int64_t)kj * HW));
+                        float pr[VEC];
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) pr[e] = Elem<T>::to_f32(lane_of<V, T, VEC>(rv, e)) * gr[e];
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j) {
+                            const int src = j - dc;  // column of the source pixel, relative to w
+                            const int m = floor_div(src, VEC);
+                            float v = lane_from(pr[src - m * VEC], m);
+                            if (m != 0) v = src_ok[m + LM] ? v : 0.f;
+                            acc[j] += v;
+                        }
                     }
                 }
             }
-        }
-        if constexpr (WANT_DX && !LS) {
-            if (!active) continue;
-            // The source runs of one kernel row (K = 5, or 8-wide runs) or of the whole
-            // dilation are issued together, without holding all 3K^2 in registers.
-            constexpr int CH = (K <= 3 && VEC <= 4) ? KK : K;
-#pragma unroll 1
-            for (int t0 = 0; t0 < KK; t0 += CH) {
+        } else {
+            if (WANT_DK && active) {
+                float gv[VEC];
 #pragma unroll
-                for (int j = 0; j < CH; ++j) {
-                    const int t = t0 + j;
+                for (int k = 0; k < VEC; ++k) gv[k] = WANT_DX ? gs[ctr + k] : Elem<T>::to_f32(gbp[pix + k]);
+#pragma unroll
+                for (int t = 0; t < KK; ++t) {
                     const int ki = t / K, kj = t % K;
-                    const int dr = (ki - r) * D, dc = (kj - r) * D;
-                    const int hs = h - dr;
-                    const bool hok = hs >= 0 && hs < H;
-                    const int64_t plane = (int64_t)(b * C + c) * KK + t;
-                    float tv[VEC];
-                    load_run<T, VEC>(tp + plane * HW + (int64_t)(hok ? hs : 0) * W, w - dc, W, hok, aligned != 0,
-                                     tv);
-                    const float *gsn = gs + ctr - dr * LW - dc;
+                    const float *xn = xs + ctr + (ki - r) * D * LW + (kj - r) * D;
+                    V dv;
 #pragma unroll
-                    for (int k = 0; k < VEC; ++k) acc[k] += tv[k] * gsn[k];
+                    for (int k = 0; k < VEC; ++k) set_lane<V, T, VEC>(dv, k, Elem<T>::from_f32(gv[k] * xn[k]));
+                    const int64_t plane = (int64_t)(b * C + c) * KK + t;
+                    __builtin_nontemporal_store(dv, (V *)(dkp + plane * HW + pix));
+                }
+            }
+            if constexpr (WANT_DX) {
+                if (!active) continue;
+                // The source runs of one kernel row (K = 5, or 8-wide runs) or of the whole
+                // dilation are issued together, without holding all 3K^2 in registers.
+                constexpr int CH = (K <= 3 && VEC <= 4) ? KK : K;
+#pragma unroll 1
+                for (int t0 = 0; t0 < KK; t0 += CH) {
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        const int t = t0 + j;
+                        const int ki = t / K, kj = t % K;
+                        const int dr = (ki - r) * D, dc = (kj - r) * D;
+                        const int hs = h - dr;
+                        const bool hok = hs >= 0 && hs < H;
+                        const int64_t plane = (int64_t)(b * C + c) * KK + t;
+                        float tv[VEC];
+                        load_run<T, VEC>(tp + plane * HW + (int64_t)(hok ? hs : 0) * W, w - dc, W, hok, aligned != 0,
+                                         tv);
+                        const float *gsn = gs + ctr - dr * LW - dc;
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) acc[k] += tv[k] * gsn[k];
+                    }
                 }
             }
         }
@@ -215,9 +264,9 @@ static hipError_t launch_filter_bwd_t(const void *x, const void *taps, const voi
     if (LS && TW < W) return hipErrorInvalidValue;
     const int TH = 256 / (TW / VEC) > 0 ? 256 / (TW / VEC) : 1;
     constexpr int HALO = 5 * ((K - 1) / 2);
-    constexpr int PADC = (HALO + 3) & ~3;
+    constexpr int PADC = LS ? 0 : (HALO + 3) & ~3;
     const size_t planes = (DK ? 1 : 0) + (DX ? 1 : 0);
-    const size_t lds = sizeof(float) * planes * (size_t)(TH + 2 * HALO) * (TW + 2 * PADC);
+    const size_t lds = (LS ? sizeof(T) : sizeof(float)) * planes * (size_t)(TH + 2 * HALO) * (TW + 2 * PADC);
     auto kern = filter_bwd_kernel<T, K, VEC, DX, DK, LS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -237,9 +286,12 @@ static hipError_t launch_filter_bwd_t(const void *x, const void *taps, const voi
 template <typename T, int K, int VEC>
 static hipError_t launch_filter_bwd_v(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N,
                                       int C, int H, int W, bool al, hipStream_t stream) {
-    if (gx == nullptr)
+    // Lane shifts need the row in one tile (and, for dX, vector-aligned tap runs).
+    if (gx == nullptr) {
+        if (W <= 64 * VEC)
+            return launch_filter_bwd_t<T, K, VEC, false, true, true>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
         return launch_filter_bwd_t<T, K, VEC, false, true, false>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
-    // Lane shifts need the row in one tile and vector-aligned tap runs.
+    }
     const bool ls = W <= 64 * VEC && (uintptr_t)taps % (VEC * sizeof(T)) == 0;
     if (gtaps != nullptr) {
         if (ls) return launch_filter_bwd_t<T, K, VEC, true, true, true>(x, taps, gout, gx, gtaps, N, C, H, W, al, stream);
