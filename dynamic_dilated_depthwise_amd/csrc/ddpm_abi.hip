@@ -35,7 +35,13 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-int status_of(hipError_t e) { return e == hipSuccess ? DDPM_OK : DDPM_ERR_HIP; }
+// The launchers refuse, before enqueueing anything, grids beyond the hardware's
+// workgroup-count limit with hipErrorInvalidConfiguration: that is a shape this
+// library does not support, not a runtime failure.
+int status_of(hipError_t e) {
+    if (e == hipSuccess) return DDPM_OK;
+    return e == hipErrorInvalidConfiguration ? DDPM_ERR_UNSUPPORTED : DDPM_ERR_HIP;
+}
 
 }  // namespace
 

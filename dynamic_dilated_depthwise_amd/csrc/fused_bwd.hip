@@ -720,11 +720,20 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
                                void *gx, void *gy, float *dwp, float *dbp, int S, int N, int C, int H, int W, bool al,
                                hipStream_t stream) {
     const int iA = al ? 1 : 0;
+    // (b, t) pairs per dW workgroup: bf16 token runs are twice as long, so fewer
+    // pairs keep the prefetched operands inside the register budget.
+    constexpr int CG = Elem<T>::is_bf16 ? 2 : 4;
+    constexpr int NCOMBO = 3 * K * K;
+    // Every grid is checked before the first launch, so a refused call writes nothing.
+    const int64_t nblk_dx = (int64_t)((W + kCols - 1) / kCols) * ((H + kRows - 1) / kRows) * N * ((C + 15) / 16);
+    const int64_t nblk_dy = (int64_t)((W + kCols - 1) / kCols) * H * N * ((C + 63) / 64);
+    const int64_t nblk_dw = (int64_t)((NCOMBO + CG - 1) / CG) * ((C + 15) / 16) * ((C + 63) / 64) * S;
+    if ((gx != nullptr && nblk_dx > 0x7fffffffLL) || (gy != nullptr && nblk_dy > 0x7fffffffLL) ||
+        (dwp != nullptr && nblk_dw > 0x7fffffffLL))
+        return hipErrorInvalidConfiguration;
     // dX
     if (gx != nullptr) {
-        const int64_t nblk = (int64_t)((W + kCols - 1) / kCols) * ((H + kRows - 1) / kRows) * N * ((C + 15) / 16);
-        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        const dim3 grid((unsigned)nblk);
+        const dim3 grid((unsigned)nblk_dx);
         const int nq = (C + Gen<T>::CH - 1) / Gen<T>::CH;
         auto args = [&](auto kern) {
             hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)y, (const T *)wg, (const T *)bg,
@@ -741,9 +750,7 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     }
     // dY
     if (gy != nullptr) {
-        const int64_t nblk = (int64_t)((W + kCols - 1) / kCols) * H * N * ((C + 63) / 64);
-        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        const dim3 grid((unsigned)nblk);
+        const dim3 grid((unsigned)nblk_dy);
         const int mb = (C >= 64) ? 4 : (C + 15) / 16;
         auto args = [&](auto kern) {
             hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)x, (const T *)wg, (const T *)gout,
@@ -757,11 +764,7 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     }
     // dW / db partials
     if (dwp != nullptr) {
-        // (b, t) pairs per workgroup: bf16 token runs are twice as long, so fewer
-        // pairs keep the prefetched operands inside the register budget.
-        constexpr int CG = Elem<T>::is_bf16 ? 2 : 4;
-        constexpr int NCOMBO = 3 * K * K;
-        const dim3 grid((unsigned)(((NCOMBO + CG - 1) / CG) * ((C + 15) / 16) * ((C + 63) / 64) * S));
+        const dim3 grid((unsigned)nblk_dw);
         const int nb = (C >= 64) ? 4 : (C + 15) / 16;
         auto args = [&](auto kern) {
             hipLaunchKernelGGL(kern, grid, dim3(64 * kDwWaves), 0, stream, (const T *)x, (const T *)y, (const T *)gout, dwp, dbp,

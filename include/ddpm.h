@@ -39,10 +39,13 @@
  *   copy of x.
  * Errors.  Every function validates all arguments before it enqueues anything;
  *   a call that fails validation writes nothing.
- *     DDPM_ERR_INVALID_ARG  a null pointer, N, C, H or W < 1, H*W >= 2^31,
- *                           C > DDPM_MAX_C, an unknown dtype, or
+ *     DDPM_ERR_INVALID_ARG  a null pointer, a pointer not aligned to its element,
+ *                           N, C, H or W < 1, H*W or N*H*W >= 2^31,
+ *                           C > DDPM_MAX_C, an unknown dtype, an output that
+ *                           overlaps another tensor of the call, or
  *                           num_partials outside [1, DDPM_MAX_PARTIALS];
- *     DDPM_ERR_UNSUPPORTED  K not in {1, 3, 5} (the dilation set is fixed);
+ *     DDPM_ERR_UNSUPPORTED  K not in {1, 3, 5} (the dilation set is fixed), or a
+ *                           shape whose grid exceeds 2^31 - 1 workgroups;
  *     DDPM_ERR_HIP          a HIP launch or attribute call failed.
  *   No C++ exception crosses this interface.  Calls are re-entrant and
  *   thread-safe.
