@@ -1,0 +1,360 @@
+// bwd_dx.hip -- dX of the fused training backward, tap recompute + gather (gfx950).
+//
+// Operation (page "lartpang/DynamicConvolutionOperator", section
+// "CUDA Flash 式融合训练": the backward recomputes the taps instead of storing
+// them):
+//     dX[c, q] = G_x[c, q] + sum_{b,t} T[o(b,c,t), q - d_bt] * G_b[c, q - d_bt],
+//     T[o, p]  = bias[o] + sum_c' W[o, c'] y[c', p].
+// For every (b, t) the generator block is run on y at the shifted pixels q - d_bt,
+// so the lane that owns output pixel q receives the tap applied at its source
+// pixel; it is multiplied by G_b at that same pixel (zero outside the image, which
+// also removes the bias-only taps recomputed there).  A gather: every dX element
+// is stored once, no atomics, no halo recompute.
+//
+// Workgroup = one 64-pixel row segment x 64 output channels; wave v owns the
+// 16-channel block 16v (MFMA rows = 16 channels of one (b, t) pair, columns = 16
+// lanes x 4 adjacent pixels, as in the fused forward).  All four waves need the
+// same B operand -- y at the shifted segment, every input channel -- so it is
+// staged once per (tap, 64-channel chunk) in LDS, double-buffered: the next
+// stage's y, weight fragments and G_b are loaded while the current stage's MFMAs
+// run, with one barrier per stage.
+//   float32: LDS rows [channel][pixel], padded to 68 floats so that the staging
+//     writes and the 16-byte fragment reads are free of bank conflicts;
+//   bfloat16: LDS rows [pixel][channel] (the MFMA operand is 8 consecutive
+//     channels of one pixel), 16-byte channel chunks XOR-swizzled by pixel/4 so
+//     the lanes of a fragment read hit distinct banks.
+#include "gen_mma.hpp"
+#include "launchers.hpp"
+
+namespace ddpm {
+namespace {
+
+constexpr int kSeg = 64;    // pixels per row segment (16 lanes x 4)
+constexpr int kChunk = 64;  // input channels per stage
+constexpr int kOutCh = 64;  // output channels per workgroup (16 per wave)
+
+template <typename T> struct DxStage;
+
+template <> struct DxStage<float> {
+    static constexpr int ROW = kSeg + 4;      // floats per staged channel row
+    static constexpr int ELEMS = kChunk * ROW;
+    static constexpr int SUB = 4;             // 16-channel MFMA chunks per stage
+    struct Regs { f32x4 v[4]; };
+
+    // Thread tid stages channel tid/4 of the chunk, pixels 16*(tid%4) .. +15 of the
+    // shifted segment starting at column ws0.
+    __device__ __forceinline__ static void load(Regs &R, const float *__restrict__ yn, int c_first, int C,
+                                                int64_t HW, int64_t rowoff, int ws0, int W, bool row_ok,
+                                                bool fast, bool al) {
+        const int c = c_first + (threadIdx.x >> 2);
+        const int px = ws0 + 16 * (threadIdx.x & 3);
+        const float *row = yn + (int64_t)(c < C ? c : 0) * HW + rowoff;
+        const bool al4 = al && ((px & 3) == 0);  // 16-byte aligned runs (rows are, when al)
+        if (fast) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R.v[i] = load4_unchecked(row, px + 4 * i, al4, true, false);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R.v[i] = load4_row(row, px + 4 * i, W, row_ok && c < C, al4);
+        }
+    }
+    __device__ __forceinline__ static void store(float *__restrict__ buf, const Regs &R) {
+        float *p = buf + (threadIdx.x >> 2) * ROW + 16 * (threadIdx.x & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(f32x4 *)(p + 4 * i) = R.v[i];
+    }
+    // B fragment of MFMA chunk `sub`: v[s][pb] = y[16 sub + 4g + s][4j + pb].
+    __device__ __forceinline__ static Gen<float>::BFrag frag(const float *__restrict__ buf, int sub, int g, int j) {
+        Gen<float>::BFrag b;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b.v[s] = *(const f32x4 *)(buf + (16 * sub + 4 * g + s) * ROW + 4 * j);
+        return b;
+    }
+};
+
+template <> struct DxStage<bf16_t> {
+    static constexpr int ELEMS = kSeg * kChunk;  // [pixel][64 channels], 128-byte rows
+    static constexpr int SUB = 2;                // 32-channel MFMA chunks per stage
+    struct Regs { u16x4 v[4]; };                 // v[channel i][pixel p]
+
+    __device__ __forceinline__ static int slot(int P, int chunk) { return P * kChunk + 8 * (chunk ^ ((P >> 2) & 7)); }
+
+    // Raw bits of row[px .. px+3].  fast: in range (px >= 1 when odd); al4: 8-byte
+    // aligned run; row4: the row start is 4-byte aligned.  Otherwise zero outside
+    // [0, W) or when !ok.
+    __device__ __forceinline__ static u16x4 run4(const bf16_t *__restrict__ row, int px, int W, bool ok, bool fast,
+                                                 bool al4, bool row4, bool odd) {
+        if (fast) {
+            if (al4) return *(const u16x4 *)(row + px);
+            if (row4 && !odd) return __builtin_bit_cast(u16x4, *(const u32x2_a4 *)(row + px));
+            if (row4) {
+                const u32x2_a4 d = *(const u32x2_a4 *)(row + px - 1);
+                u16x4 u;
+                u[0] = (uint16_t)(d[0] >> 16); u[1] = (uint16_t)d[1]; u[2] = (uint16_t)(d[1] >> 16);
+                u[3] = row[px + 3];
+                return u;
+            }
+        }
+        u16x4 u = {0, 0, 0, 0};
+        if (!ok) return u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int ww = px + k;
+            if (fast || (ww >= 0 && ww < W)) u[k] = row[ww];
+        }
+        return u;
+    }
+
+    // Thread tid stages channels 4*(tid/16) .. +3 of the chunk, pixels 4*(tid%16) .. +3.
+    __device__ __forceinline__ static void load(Regs &R, const bf16_t *__restrict__ yn, int c_first, int C,
+                                                int64_t HW, int64_t rowoff, int ws0, int W, bool row_ok,
+                                                bool fast, bool al) {
+        const int px = ws0 + 4 * (threadIdx.x & 15);
+        const bool odd = (ws0 & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c_first + 4 * (threadIdx.x >> 4) + i;
+            const bf16_t *row = yn + (int64_t)(c < C ? c : 0) * HW + rowoff;
+            R.v[i] = run4(row, px, W, row_ok && c < C, fast, al && ((px & 3) == 0), al, odd);
+        }
+    }
+    __device__ __forceinline__ static void store(bf16_t *__restrict__ buf, const Regs &R) {
+        const int c4 = 4 * (threadIdx.x >> 4);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int P = 4 * (threadIdx.x & 15) + p;
+            u16x4 u;
+            u[0] = R.v[0][p]; u[1] = R.v[1][p]; u[2] = R.v[2][p]; u[3] = R.v[3][p];
+            *(u16x4 *)(buf + slot(P, c4 >> 3) + (c4 & 4)) = u;
+        }
+    }
+    // B fragment of MFMA chunk `sub`: v[pb] = y[32 sub + 8g + e][4j + pb], e = 0..7.
+    __device__ __forceinline__ static Gen<bf16_t>::BFrag frag(const bf16_t *__restrict__ buf, int sub, int g,
+                                                              int j) {
+        Gen<bf16_t>::BFrag b;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb)
+            b.v[pb] = __builtin_bit_cast(bf16x8, *(const u16x8 *)(buf + slot(4 * j + pb, 4 * sub + g)));
+        return b;
+    }
+};
+
+template <typename T, int K>
+__global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y, const T *__restrict__ wg,
+                                                        const T *__restrict__ bg, const T *__restrict__ gout,
+                                                        T *__restrict__ gx, int C, int H, int W, int al) {
+    using G = Gen<T>;
+    using S = DxStage<T>;
+    constexpr int r = (K - 1) / 2;
+    constexpr int KK = K * K;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    // logical tile order: channel group fastest, then column segment, row, image
+    const int ncg = (C + kOutCh - 1) / kOutCh;
+    const int nseg = (W + kSeg - 1) / kSeg;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int cg0 = (L % ncg) * kOutCh;
+    L /= ncg;
+    const int w0 = (L % nseg) * kSeg;
+    L /= nseg;
+    const int h = L % H;
+    const int n = L / H;
+    const int c0 = cg0 + 16 * wave;             // this wave's output channel block
+    const bool wave_on = c0 < C;                // wave-uniform
+    const int w = w0 + 4 * j;
+    const int cA = c0 + j;                      // generator row channel this lane supplies
+    const int64_t HW = (int64_t)H * W;
+    const bool aligned4 = al != 0;
+    const bool cvec = Elem<T>::is_bf16 ? (al != 0 && (C & 7) == 0) : (al != 0 && (C & 3) == 0);
+    // All 16 channels of the block exist, weights are vector-aligned, and 32-bit lane
+    // offsets address a 16-plane G slice (wave-uniform).
+    const bool full = (c0 + 16 <= C) && cvec && HW < (int64_t(1) << 26);
+    const int HWi = (int)(full ? HW : 0);
+    const T *__restrict__ yn = y + (int64_t)n * C * HW;
+    const T *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
+    const int nqq = (C + kChunk - 1) / kChunk;
+    const int nstage = 3 * KK * nqq;
+
+    __shared__ float bl[3 * KK * kOutCh];  // bl[(b*KK + t)*64 + ch] = bias[(b*C + cg0 + ch)*KK + t]
+    __shared__ __align__(16) T stage[2][S::ELEMS];
+    for (int i = threadIdx.x; i < 3 * KK * kOutCh; i += blockDim.x) {
+        const int combo = i / kOutCh;
+        const int c = cg0 + (i - combo * kOutCh);
+        const int b = combo / KK;
+        const int t = combo - b * KK;
+        bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+    }
+
+    struct Shift {
+        int b, t, hs, dc;
+        bool row_ok;
+    };
+    auto shift_of = [&](int s) {
+        Shift sh;
+        const int combo = s / nqq;
+        sh.b = combo / KK;
+        sh.t = combo - sh.b * KK;
+        const int D = dilation(sh.b);
+        const int ki = sh.t / K;
+        const int kj = sh.t - ki * K;
+        sh.hs = h - (ki - r) * D;
+        sh.dc = (kj - r) * D;
+        sh.row_ok = sh.hs >= 0 && sh.hs < H;
+        return sh;
+    };
+    // y of stage s (shifted segment, one 64-channel chunk) into staging registers
+    auto load_stage = [&](int s, typename S::Regs &R) {
+        const Shift sh = shift_of(s);
+        const int qq = s % nqq;
+        const int ws0 = w0 - sh.dc;
+        const int64_t rowoff = (int64_t)(sh.row_ok ? sh.hs : 0) * W;
+        const bool fast = (kChunk * qq + kChunk <= C) && sh.row_ok && ws0 - (ws0 & 1) >= 0 && ws0 + kSeg <= W;
+        S::load(R, yn, kChunk * qq, C, HW, rowoff, ws0, W, sh.row_ok, fast, aligned4);
+    };
+    // weight fragments of stage s for this wave's 16 generator rows
+    auto load_A = [&](int s, typename G::AFrag (&a)[S::SUB]) {
+        const Shift sh = shift_of(s);
+        const int qq = s % nqq;
+#pragma unroll
+        for (int u = 0; u < S::SUB; ++u) {
+            const int q = S::SUB * qq + u;  // MFMA chunk of G::CH input channels
+            if (full && kChunk * qq + kChunk <= C) {
+                a[u] = G::load_A_off(wg + ((int64_t)sh.b * C * KK + sh.t) * C, cA * KK * C + G::CH * q +
+                                                                                    (G::CH / 4) * g);
+            } else {
+                const T *arow = cA < C ? wg + ((int64_t)(sh.b * C + cA) * KK + sh.t) * C : nullptr;
+                a[u] = G::load_A(arow, q, g, C, cvec);
+            }
+        }
+    };
+    // G_b at the source pixels of the tap of stage s: gs[v][pb] for channel c0+4g+v
+    auto load_G = [&](int s, f32x4 (&gs)[4]) {
+        const Shift sh = shift_of(s);
+        const int ws = w - sh.dc;
+        const int odd = sh.dc & 1;
+        const bool al_s = aligned4 && ((sh.dc & 3) == 0);
+        const int64_t rowoff = (int64_t)(sh.row_ok ? sh.hs : 0) * W;
+        if (full && sh.row_ok && w0 - sh.dc - odd >= 0 && w0 + kSeg - 1 - sh.dc < W) {  // wave-uniform
+            const T *gbase = gn + (int64_t)((1 + sh.b) * C + c0) * HW + rowoff;
+            const int goff = 4 * g * HWi + ws;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) gs[v] = load4_unchecked(gbase + (int64_t)v * HWi, goff, al_s, aligned4, odd);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int c = c0 + 4 * g + v;
+                gs[v] = load4_row(gn + (int64_t)((1 + sh.b) * C + (c < C ? c : 0)) * HW + rowoff, ws, W,
+                                  sh.row_ok && c < C, al_s);
+            }
+        }
+    };
+
+    typename S::Regs R;
+    load_stage(0, R);
+    S::store(stage[0], R);
+    typename G::AFrag acur[S::SUB];
+    f32x4 gcur[4], gnext[4];
+    if (wave_on) {
+        load_A(0, acur);
+        load_G(0, gcur);
+    }
+    float dacc[4][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) dacc[v][pb] = 0.f;
+    f32x4 acc[4];
+    __syncthreads();
+
+#pragma unroll 1
+    for (int s = 0; s < nstage; ++s) {
+        const bool more = s + 1 < nstage;
+        const int qq = s % nqq;
+        typename G::AFrag anext[S::SUB];
+        if (more) {
+            load_stage(s + 1, R);
+            if (wave_on) {
+                load_A(s + 1, anext);
+                if ((s + 1) % nqq == 0) load_G(s + 1, gnext);
+            }
+        }
+        if (wave_on) {
+            if (qq == 0) {
+                const f32x4 bias = *(const f32x4 *)(bl + (s / nqq) * kOutCh + 16 * wave + 4 * g);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc[pb] = bias;
+            }
+            const T *buf = stage[s & 1];
+            const int left = C - kChunk * qq;
+            const int nsub = left >= kChunk ? S::SUB : (left + G::CH - 1) / G::CH;
+#pragma unroll
+            for (int u = 0; u < S::SUB; ++u)
+                if (u < nsub) G::mma(acc, acur[u], S::frag(buf, u, g, j));
+            if (qq == nqq - 1) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += Elem<T>::quant(acc[pb][v]) * gcur[v][pb];
+                if (more) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) gcur[v] = gnext[v];
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < S::SUB; ++u) acur[u] = anext[u];
+            }
+        }
+        if (more) S::store(stage[(s + 1) & 1], R);
+        __syncthreads();
+    }
+
+    if (!wave_on) return;
+    const int64_t rowoff = (int64_t)h * W;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int c = c0 + 4 * g + v;
+        if (c >= C || w >= W) continue;
+        const f32x4 gxs = load4_row(gn + (int64_t)c * HW + rowoff, w, W, true, aligned4);
+        f32x4 o;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) o[pb] = dacc[v][pb] + gxs[pb];
+        store4_row(gx + ((int64_t)n * C + c) * HW + rowoff, w, W, o, aligned4);
+    }
+}
+
+template <typename T, int K>
+hipError_t launch_dx_t(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N, int C, int H,
+                       int W, bool al, hipStream_t stream) {
+    const int64_t nblk = bwd_dx_blocks(N, C, H, W);
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dx_kernel<T, K>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T *)y,
+                       (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_dx_blocks(int N, int C, int H, int W) {
+    return (int64_t)N * H * ((W + kSeg - 1) / kSeg) * ((C + kOutCh - 1) / kOutCh);
+}
+
+hipError_t launch_bwd_dx(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N, int C,
+                         int H, int W, int K, bool bf16, bool al, hipStream_t stream) {
+    if (bf16) {
+        switch (K) {
+            case 1: return launch_dx_t<bf16_t, 1>(y, wg, bg, gout, gx, N, C, H, W, al, stream);
+            case 3: return launch_dx_t<bf16_t, 3>(y, wg, bg, gout, gx, N, C, H, W, al, stream);
+            default: return launch_dx_t<bf16_t, 5>(y, wg, bg, gout, gx, N, C, H, W, al, stream);
+        }
+    }
+    switch (K) {
+        case 1: return launch_dx_t<float, 1>(y, wg, bg, gout, gx, N, C, H, W, al, stream);
+        case 3: return launch_dx_t<float, 3>(y, wg, bg, gout, gx, N, C, H, W, al, stream);
+        default: return launch_dx_t<float, 5>(y, wg, bg, gout, gx, N, C, H, W, al, stream);
+    }
+}
+
+}  // namespace ddpm

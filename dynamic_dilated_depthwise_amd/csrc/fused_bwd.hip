@@ -19,169 +19,6 @@ namespace ddpm {
 constexpr int kRows = 4;   // one row per wave
 constexpr int kCols = 64;  // 16 lanes x 4 pixels
 
-// ============================================================================ dX
-// Same tile as the fused forward.  For every (b, t) the generator block is run
-// with y read at the pixel shifted by -d_bt, so each lane holds the tap that
-// was applied at the source pixel q - d_bt; it is multiplied by G_b at that
-// same source pixel.  Zero-padded G kills every term whose source pixel lies
-// outside the image (the recomputed tap there would be the bias alone).
-template <typename T, int K, int KQ>
-__global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y, const T *__restrict__ wg,
-                                                        const T *__restrict__ bg, const T *__restrict__ gout,
-                                                        T *__restrict__ gx, int C, int H, int W, int al) {
-    using G = Gen<T>;
-    constexpr int r = (K - 1) / 2;
-    constexpr int KK = K * K;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int g = lane >> 4;
-    const int j = lane & 15;
-    const int nCB = (C + 15) >> 4;
-    // logical tile order: channel block fastest, then column tile, row band, image
-    const int ncolt = (W + kCols - 1) / kCols;
-    const int nbands = (H + kRows - 1) / kRows;
-    int L = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int c0 = (L % nCB) * 16;
-    L /= nCB;
-    const int w = (L % ncolt) * kCols + 4 * j;
-    L /= ncolt;
-    const int h = (L % nbands) * kRows + wave;
-    const int n = L / nbands;
-    // bias slice: bl[(b*KK + t)*16 + ch] = bias[(b*C + c0 + ch)*KK + t]
-    __shared__ float bl[3 * KK * 16];
-    for (int i = threadIdx.x; i < 3 * KK * 16; i += blockDim.x) {
-        const int combo = i >> 4;
-        const int c = c0 + (i & 15);
-        const int b = combo / KK;
-        const int t = combo - b * KK;
-        bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
-    }
-    __syncthreads();
-    if (h >= H) return;  // no barriers below
-    const int64_t HW = (int64_t)H * W;
-    const bool aligned4 = al != 0;
-    const bool cvec = Elem<T>::is_bf16 ? (al != 0 && (C & 7) == 0) : (al != 0 && (C & 3) == 0);
-    const T *__restrict__ yn = y + (int64_t)n * C * HW;
-    const T *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
-    const int nq = KQ > 0 ? KQ : (C + G::CH - 1) / G::CH;
-    const int cA = c0 + j;
-    const int w0 = w - 4 * j;  // tile's first column (wave-uniform)
-    // Wave-uniform: all 16 channels exist, every weight chunk is whole and vector-aligned.
-    // (KQ chunks must cover exactly C channels: the fp32 KQ=4 instance also serves C = 48;
-    // the streamed KQ=0 instance only visits chunks q < nq.)
-    // Fast paths also address a chunk as uniform base + 32-bit lane offset (< 32 planes).
-    const bool full = (c0 + 16 <= C) && cvec && (C % G::CH == 0) && (KQ == 0 || KQ * G::CH == C) &&
-                      HW < (int64_t(1) << 26);
-    const int HWi = (int)(full ? HW : 0);
-    const int aoff = cA * KK * C + (G::CH / 4) * g;  // lane's offset inside a (b, t) weight slice
-
-    float dacc[4][4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) dacc[v][pb] = 0.f;
-
-    // Operands of one (tap, channel chunk) step: a generator-row fragment and y at
-    // the tap's shifted pixels.  The loop runs over (tap t, chunk q) steps with the
-    // next step's loads issued before the current step's MFMAs.
-    struct Step {
-        typename G::AFrag a;
-        typename G::BFrag y;
-    };
-    const int nsteps_q = nq;
-#pragma unroll
-    for (int b = 0; b < 3; ++b) {
-        const int D = dilation(b);
-        auto fetch = [&](int t, int q, Step &st) {
-            const int ki = t / K;
-            const int kj = t - ki * K;
-            const int hs = h - (ki - r) * D;
-            const int dc = (kj - r) * D;
-            const bool rs_ok = hs >= 0 && hs < H;
-            const int64_t rowoff = (int64_t)(rs_ok ? hs : 0) * W;
-            // wave-uniform: the shifted row exists and all 64 shifted columns are inside it
-            const int odd = dc & 1;
-            if (full && rs_ok && w0 - dc - odd >= 0 && w0 + kCols - 1 - dc < W) {
-                st.a = G::load_A_off(wg + ((int64_t)b * C * KK + t) * C, aoff + G::CH * q);
-                st.y = G::load_B_off(yn + (int64_t)(G::CH * q) * HW + rowoff, (G::CH / 4) * g * HWi + w - dc, HWi,
-                                     aligned4 && ((dc & 3) == 0), aligned4, odd);
-            } else {
-                const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
-                st.a = G::load_A(arow, q, g, C, cvec);
-                st.y = G::load_B(yn, q, g, C, HW, rowoff, w - dc, W, rs_ok, aligned4 && ((dc & 3) == 0));
-            }
-        };
-        Step cur;
-        fetch(0, 0, cur);
-#pragma unroll 1
-        for (int t = 0; t < KK; ++t) {
-            const int ki = t / K;
-            const int kj = t - ki * K;
-            const int hs = h - (ki - r) * D;
-            const int ws = w - (kj - r) * D;
-            const bool rs_ok = hs >= 0 && hs < H;
-            const bool al_s = aligned4 && ((((kj - r) * D) & 3) == 0);
-            const int64_t rowoff = (int64_t)(rs_ok ? hs : 0) * W;
-            // G_b at the source pixels (consumed after the MFMAs)
-            f32x4 gs[4];
-            const int dcs = (kj - r) * D;
-            const int odd = dcs & 1;
-            if (full && rs_ok && w0 - dcs - odd >= 0 && w0 + kCols - 1 - dcs < W) {  // wave-uniform
-                const T *gbase = gn + (int64_t)((1 + b) * C + c0) * HW + rowoff;  // uniform
-                const int goff = 4 * g * HWi + ws;                                  // lane
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    gs[v] = load4_unchecked(gbase + (int64_t)v * HWi, goff, al_s, aligned4, odd);
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int c = c0 + 4 * g + v;
-                    gs[v] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, ws, W,
-                                      rs_ok && c < C, al_s);
-                }
-            }
-            const f32x4 bias = *(const f32x4 *)(bl + (b * KK + t) * 16 + 4 * g);
-            f32x4 acc[4];
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) acc[pb] = bias;
-            if constexpr (KQ > 0) {
-#pragma unroll
-                for (int q = 0; q < KQ; ++q) {
-                    Step nxt;
-                    if (q + 1 < KQ) fetch(t, q + 1, nxt);
-                    else if (t + 1 < KK) fetch(t + 1, 0, nxt);
-                    G::mma(acc, cur.a, cur.y);
-                    cur = nxt;
-                }
-            } else {
-                for (int q = 0; q < nsteps_q; ++q) {
-                    Step nxt;
-                    if (q + 1 < nsteps_q) fetch(t, q + 1, nxt);
-                    else if (t + 1 < KK) fetch(t + 1, 0, nxt);
-                    G::mma(acc, cur.a, cur.y);
-                    cur = nxt;
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += Elem<T>::quant(acc[pb][v]) * gs[v][pb];
-        }
-    }
-
-    const int64_t rowoff = (int64_t)h * W;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int c = c0 + 4 * g + v;
-        if (c >= C) continue;
-        const f32x4 gxs = load4_row(gn + (int64_t)c * HW + rowoff, w, W, true, aligned4);
-        f32x4 o;
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) o[pb] = dacc[v][pb] + gxs[pb];
-        store4_row(gx + ((int64_t)n * C + c) * HW + rowoff, w, W, o, aligned4);
-    }
-}
-
 // ============================================================================ dY
 // dY = W^T dK as an MFMA product: rows = output channels c' (16 per block, MB
 // blocks), columns = one 64-pixel row segment (4 pixels per lane), contraction
@@ -725,27 +562,15 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     constexpr int CG = Elem<T>::is_bf16 ? 2 : 4;
     constexpr int NCOMBO = 3 * K * K;
     // Every grid is checked before the first launch, so a refused call writes nothing.
-    const int64_t nblk_dx = (int64_t)((W + kCols - 1) / kCols) * ((H + kRows - 1) / kRows) * N * ((C + 15) / 16);
+    const int64_t nblk_dx = bwd_dx_blocks(N, C, H, W);
     const int64_t nblk_dy = (int64_t)((W + kCols - 1) / kCols) * H * N * ((C + 63) / 64);
     const int64_t nblk_dw = (int64_t)((NCOMBO + CG - 1) / CG) * ((C + 15) / 16) * ((C + 63) / 64) * S;
     if ((gx != nullptr && nblk_dx > 0x7fffffffLL) || (gy != nullptr && nblk_dy > 0x7fffffffLL) ||
         (dwp != nullptr && nblk_dw > 0x7fffffffLL))
         return hipErrorInvalidConfiguration;
-    // dX
+    // dX (bwd_dx.hip)
     if (gx != nullptr) {
-        const dim3 grid((unsigned)nblk_dx);
-        const int nq = (C + Gen<T>::CH - 1) / Gen<T>::CH;
-        auto args = [&](auto kern) {
-            hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)y, (const T *)wg, (const T *)bg,
-                               (const T *)gout, (T *)gx, C, H, W, iA);
-        };
-        if (nq == 1) args(bwd_dx_kernel<T, K, 1>);
-        else if (nq == 2) args(bwd_dx_kernel<T, K, 2>);
-        else if constexpr (!Elem<T>::is_bf16) {
-            if (nq <= 4) args(bwd_dx_kernel<T, K, 4>);
-            else args(bwd_dx_kernel<T, K, 0>);
-        } else args(bwd_dx_kernel<T, K, 0>);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_bwd_dx(y, wg, bg, gout, gx, N, C, H, W, K, Elem<T>::is_bf16, al, stream);
         if (e != hipSuccess) return e;
     }
     // dY

@@ -20,6 +20,11 @@ hipError_t launch_fused_bwd(const void *x, const void *y, const void *wg, const 
                             void *gx, void *gy, float *dw_part, float *db_part, int S, int N, int C, int H,
                             int W, int K, bool bf16, bool aligned4, hipStream_t stream);
 
+// dX of the fused backward (one kernel); bwd_dx_blocks is its grid size.
+int64_t bwd_dx_blocks(int N, int C, int H, int W);
+hipError_t launch_bwd_dx(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N, int C,
+                         int H, int W, int K, bool bf16, bool al, hipStream_t stream);
+
 // gx or gtaps may be null: that output is skipped (not both).
 hipError_t launch_filter_bwd(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N, int C,
                              int H, int W, int K, bool bf16, int vec, bool aligned, hipStream_t stream);
