@@ -201,59 +201,73 @@ __device__ __forceinline__ void load8_bf16_row(const bf16_t *__restrict__ row, i
     }
 }
 
-// Eight bf16 pixels w..w+7 with no bounds checks (caller: w + 7 < W, and w >= 1 when
-// w is odd).  `al16`: w % 8 == 0 with 16-byte aligned rows; `row_even`: 4-byte
-// aligned rows; `odd`: w is odd (wave-uniform).
-__device__ __forceinline__ void load8_bf16_unchecked(const bf16_t *__restrict__ row, int w, bool al16, bool row_even,
-                                                     bool odd, float (&v)[8]) {
-    if (al16) {
-        const u16x8 u = *(const u16x8_a16 *)(row + w);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = bf16_bits_to_f32(u[k]);
-    } else if (row_even && !odd) {
-        const u32x4_a4 d = *(const u32x4_a4 *)(row + w);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = __uint_as_float(d[k] << 16);
-            v[2 * k + 1] = __uint_as_float(d[k] & 0xffff0000u);
-        }
-    } else if (row_even) {
-        const u32x4_a4 d = *(const u32x4_a4 *)(row + w - 1);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = __uint_as_float(d[k] & 0xffff0000u);
-            if (k < 3) v[2 * k + 1] = __uint_as_float(d[k + 1] << 16);
-        }
-        v[7] = bf16_bits_to_f32(row[w + 7]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = bf16_bits_to_f32(row[w + k]);
+// A run of consecutive pixels of one row kept as loaded: four float32 values, or
+// eight raw bfloat16 values (which feed a bf16 MFMA operand without conversion).
+template <typename T> struct Run;
+template <> struct Run<float> {
+    static constexpr int RL = 4;
+    f32x4 v;
+    __device__ __forceinline__ float at(int k) const { return v[k]; }
+    __device__ __forceinline__ void set_raw(int k, float e) { v[k] = e; }
+    __device__ __forceinline__ static Run zero() { return Run{f32x4{0.f, 0.f, 0.f, 0.f}}; }
+    // No bounds checks (caller: w >= 0, w + 3 < W).  `wal`: w % 4 == 0 with
+    // 16-byte aligned rows.
+    __device__ __forceinline__ static Run fast(const float *__restrict__ row, int w, bool wal, bool, bool) {
+        return Run{load4_unchecked(row, w, wal, true, false)};
     }
-}
-
-// RL consecutive pixels of a row as float: 4 for float32 tensors, 8 for bf16.
-template <typename T, int RL> struct RowRun;
-template <> struct RowRun<float, 4> {
-    __device__ __forceinline__ static void load(const float *__restrict__ row, int w, int W, bool ok, bool al,
-                                                float (&v)[4]) {
-        const f32x4 t = load4_row(row, w, W, ok, al && ((w & 3) == 0));
-        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
-    }
-    // No bounds checks; `wal`: the run is vector-aligned (w % 4 == 0, aligned rows).
-    __device__ __forceinline__ static void load_fast(const float *__restrict__ row, int w, bool wal, bool, bool,
-                                                     float (&v)[4]) {
-        const f32x4 t = load4_unchecked(row, w, wal, true, false);
-        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    // Zero outside [0, W) or when !ok.  `al`: rows 16-byte aligned.
+    __device__ __forceinline__ static Run checked(const float *__restrict__ row, int w, int W, bool ok, bool al) {
+        return Run{load4_row(row, w, W, ok, al && ((w & 3) == 0))};
     }
 };
-template <> struct RowRun<bf16_t, 8> {
-    __device__ __forceinline__ static void load(const bf16_t *__restrict__ row, int w, int W, bool ok, bool,
-                                                float (&v)[8]) {
-        load8_bf16_row(row, w, W, ok, v);
+template <> struct Run<bf16_t> {
+    static constexpr int RL = 8;
+    u16x8 v;
+    __device__ __forceinline__ float at(int k) const { return bf16_bits_to_f32(v[k]); }
+    __device__ __forceinline__ void set_raw(int k, bf16_t e) { v[k] = e; }
+    __device__ __forceinline__ static Run zero() { return Run{u16x8{0, 0, 0, 0, 0, 0, 0, 0}}; }
+    // No bounds checks (caller: w + 7 < W, and w >= 1 when w is odd).  `wal`: w % 8 == 0
+    // with 16-byte aligned rows; `row_even`: 4-byte aligned rows; `odd`: w is odd.
+    __device__ __forceinline__ static Run fast(const bf16_t *__restrict__ row, int w, bool wal, bool row_even,
+                                               bool odd) {
+        Run r;
+        if (wal) {
+            r.v = *(const u16x8_a16 *)(row + w);
+        } else if (row_even && !odd) {
+            r.v = __builtin_bit_cast(u16x8, *(const u32x4_a4 *)(row + w));
+        } else if (row_even) {
+            // dwords cover w-1 .. w+6; the last pixel comes on its own
+            const u32x4_a4 d = *(const u32x4_a4 *)(row + w - 1);
+            const uint32_t e = row[w + 7];
+            u32x4_a4 o;
+            o[0] = __builtin_amdgcn_alignbit(d[1], d[0], 16);
+            o[1] = __builtin_amdgcn_alignbit(d[2], d[1], 16);
+            o[2] = __builtin_amdgcn_alignbit(d[3], d[2], 16);
+            o[3] = __builtin_amdgcn_alignbit(e, d[3], 16);
+            r.v = __builtin_bit_cast(u16x8, o);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) r.v[k] = row[w + k];
+        }
+        return r;
     }
-    __device__ __forceinline__ static void load_fast(const bf16_t *__restrict__ row, int w, bool wal, bool row_even,
-                                                     bool odd, float (&v)[8]) {
-        load8_bf16_unchecked(row, w, wal, row_even, odd, v);
+    // Zero outside [0, W) or when !ok; vector loads whenever the run is in range
+    // (chosen by the run's address).
+    __device__ __forceinline__ static Run checked(const bf16_t *__restrict__ row, int w, int W, bool ok, bool) {
+        if (!ok) return zero();
+        if (w >= 0 && w + 7 < W) {
+            const uintptr_t a = (uintptr_t)(row + w);
+            if ((a & 15) == 0) return fast(row, w, true, true, false);
+            if ((a & 3) == 0) return fast(row, w, false, true, false);
+            if (w >= 1) return fast(row, w, false, true, true);  // row + w - 1 is 4-byte aligned
+        }
+        Run r = zero();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int ww = w + k;
+            if (ww >= 0 && ww < W) r.v[k] = row[ww];
+        }
+        return r;
     }
 };
 

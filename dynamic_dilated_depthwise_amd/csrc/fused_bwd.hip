@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
     constexpr int KK = K * K;
     constexpr int NCOMBO = 3 * KK;
     constexpr bool BF = Elem<T>::is_bf16;
-    constexpr int RL = BF ? 8 : 4;  // tokens per lane per chunk
+    constexpr int RL = Run<T>::RL;  // tokens per lane per chunk
     constexpr int KC = 4 * RL;      // tokens per wave per chunk
     __shared__ float red[kDwWaves][NB * 4][64];
     __shared__ float redb[kDwWaves][4][16];
@@ -323,9 +323,9 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
     // Raw operands of one chunk: G_b and shifted x per (b, t) pair (their product is
     // the A operand dK), y per c' block (the B operand).
     struct Raw {
-        float gv[CG][RL];
-        float xv[CG][RL];
-        float yv[NB][RL];
+        Run<T> gv[CG];
+        Run<T> xv[CG];
+        Run<T> yv[NB];
     };
     // For loading, a (b, t) slot past the last pair reads the b = 0, zero-shift
     // plane (always valid); its product is zeroed by cb_valid at consumption.
@@ -358,24 +358,19 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
 #pragma unroll
             for (int cc = 0; cc < CG; ++cc) {
                 const int dc = cb_dc[cc];
-                RowRun<T, RL>::load_fast(gn + (int64_t)((1 + cb_bl[cc]) * C + cA) * HW + rowoff, w, wal, al, odd,
-                                         o.gv[cc]);
-                RowRun<T, RL>::load_fast(xn + (int64_t)cA * HW + (int64_t)(qh + cb_dr[cc]) * W, w + dc,
-                                         wal && (dc % RL == 0), al, ((qw + dc) & 1) != 0, o.xv[cc]);
+                o.gv[cc] = Run<T>::fast(gn + (int64_t)((1 + cb_bl[cc]) * C + cA) * HW + rowoff, w, wal, al, odd);
+                o.xv[cc] = Run<T>::fast(xn + (int64_t)cA * HW + (int64_t)(qh + cb_dr[cc]) * W, w + dc,
+                                        wal && (dc % RL == 0), al, ((qw + dc) & 1) != 0);
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                RowRun<T, RL>::load_fast(yn + (int64_t)(cn0 + 16 * nb + j) * HW + rowoff, w, wal, al, odd, o.yv[nb]);
+                o.yv[nb] = Run<T>::fast(yn + (int64_t)(cn0 + 16 * nb + j) * HW + rowoff, w, wal, al, odd);
             return;
         }
 #pragma unroll
-        for (int cc = 0; cc < CG; ++cc)
+        for (int cc = 0; cc < CG; ++cc) o.gv[cc] = o.xv[cc] = Run<T>::zero();
 #pragma unroll
-            for (int k = 0; k < RL; ++k) o.gv[cc][k] = o.xv[cc][k] = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int k = 0; k < RL; ++k) o.yv[nb][k] = 0.f;
+        for (int nb = 0; nb < NB; ++nb) o.yv[nb] = Run<T>::zero();
         if (in_row) {
             const int w = qw + RL * g;
             const T *xn = x + (int64_t)qn * CHW;
@@ -386,17 +381,17 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
             for (int cc = 0; cc < CG; ++cc) {
                 const int b = cb_b[cc];
                 if (b >= 0 && cA_ok) {
-                    RowRun<T, RL>::load(gn + (int64_t)((1 + b) * C + cA) * HW + rowoff, w, W, true, al, o.gv[cc]);
+                    o.gv[cc] = Run<T>::checked(gn + (int64_t)((1 + b) * C + cA) * HW + rowoff, w, W, true, al);
                     const int hs = qh + cb_dr[cc];
                     const bool hok = hs >= 0 && hs < H;
-                    RowRun<T, RL>::load(xn + (int64_t)cA * HW + (int64_t)(hok ? hs : 0) * W, w + cb_dc[cc], W, hok,
-                                        al, o.xv[cc]);
+                    o.xv[cc] = Run<T>::checked(xn + (int64_t)cA * HW + (int64_t)(hok ? hs : 0) * W, w + cb_dc[cc], W,
+                                               hok, al);
                 }
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int cp = cn0 + 16 * nb + j;
-                if (cp < C) RowRun<T, RL>::load(yn + (int64_t)cp * HW + rowoff, w, W, true, al, o.yv[nb]);
+                if (cp < C) o.yv[nb] = Run<T>::checked(yn + (int64_t)cp * HW + rowoff, w, W, true, al);
             }
         } else {
             const int64_t pf = q0 + (int64_t)g * RL;  // this lane's first token
@@ -422,15 +417,15 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
                             const int hs = hh + cb_dr[cc];
                             const int ws = ww + cb_dc[cc];
                             if (hs >= 0 && hs < H && ws >= 0 && ws < W) {
-                                o.gv[cc][k] = Elem<T>::to_f32(gn[(int64_t)((1 + b) * C + cA) * HW + pix]);
-                                o.xv[cc][k] = Elem<T>::to_f32(xn[(int64_t)cA * HW + (int64_t)hs * W + ws]);
+                                o.gv[cc].set_raw(k, gn[(int64_t)((1 + b) * C + cA) * HW + pix]);
+                                o.xv[cc].set_raw(k, xn[(int64_t)cA * HW + (int64_t)hs * W + ws]);
                             }
                         }
                     }
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         const int cp = cn0 + 16 * nb + j;
-                        if (cp < C) o.yv[nb][k] = Elem<T>::to_f32(yn[(int64_t)cp * HW + pix]);
+                        if (cp < C) o.yv[nb].set_raw(k, yn[(int64_t)cp * HW + pix]);
                     }
                 }
                 if (++ww == W) {
@@ -460,7 +455,7 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
         for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
             for (int k = 0; k < RL; ++k) {
-                a[cc][k] = o.gv[cc][k] * o.xv[cc][k] * cb_valid[cc];
+                a[cc][k] = o.gv[cc].at(k) * o.xv[cc].at(k) * cb_valid[cc];
                 dbacc[cc] += a[cc][k];
             }
         if constexpr (!BF) {
@@ -470,16 +465,11 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
                 for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
-                        acc[cc][nb] = mfma_16x16x4_f32(a[cc][k], o.yv[nb][k], acc[cc][nb]);
+                        acc[cc][nb] = mfma_16x16x4_f32(a[cc][k], o.yv[nb].at(k), acc[cc][nb]);
         } else {
-            bf16x8 bq[NB];
+            bf16x8 bq[NB];  // y is already the bf16 operand
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                uint16_t u[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) u[k] = f32_to_bf16_bits(o.yv[nb][k]);  // exact: y is bf16
-                bq[nb] = pack_bf16x8(u);
-            }
+            for (int nb = 0; nb < NB; ++nb) bq[nb] = __builtin_bit_cast(bf16x8, o.yv[nb].v);
 #pragma unroll
             for (int cc = 0; cc < CG; ++cc) {
                 uint16_t u[8];
@@ -492,8 +482,8 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
         }
     };
 
-    if constexpr (!BF) {
-        // float32: the next chunk's loads are issued before this chunk's MFMAs.
+    // The next chunk's loads are issued before this chunk's products and MFMAs.
+    {
         Raw nxt;
         if (p0 < t1) load_chunk(p0, pn, ph, pw, nxt);
         while (p0 < t1) {
@@ -501,13 +491,6 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
             advance(p0, pn, ph, pw);
             if (p0 < t1) load_chunk(p0, pn, ph, pw, nxt);
             consume(cur);
-        }
-    } else {
-        while (p0 < t1) {
-            Raw cur;
-            load_chunk(p0, pn, ph, pw, cur);
-            consume(cur);
-            advance(p0, pn, ph, pw);
         }
     }
 
