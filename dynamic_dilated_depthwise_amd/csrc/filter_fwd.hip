@@ -9,9 +9,10 @@
 //   * one workgroup = one (n, c) plane x a TH x TW pixel tile;
 //   * the x tile plus a 5*(K-1)/2 halo is staged once in LDS (as float), so every
 //     dilation's neighbourhood is read from LDS, never re-fetched from HBM;
-//   * each thread owns VEC consecutive pixels of a row and streams the taps with
-//     16-byte non-temporal loads (they are touched exactly once), and writes the
-//     four output planes with non-temporal vector stores;
+//   * each thread owns VEC = 4 consecutive pixels of a row (16-byte float32 /
+//     8-byte bfloat16 runs) and streams the taps with non-temporal vector loads
+//     (they are touched exactly once), and writes the four output planes with
+//     non-temporal vector stores;
 //   * the x block of the output is copied from the staged tile bit-exactly.
 #include "common.hpp"
 #include "launchers.hpp"
@@ -129,19 +130,10 @@ static hipError_t launch_filter_t(const void *x, const void *taps, void *out, in
 template <typename T, int K>
 static hipError_t launch_filter_k(const void *x, const void *taps, void *out, int N, int C, int H, int W,
                                   hipStream_t stream, int vec) {
-    if constexpr (Elem<T>::is_bf16) {
-        switch (vec) {
-            case 8: return launch_filter_t<T, K, 8>(x, taps, out, N, C, H, W, stream);
-            case 4: return launch_filter_t<T, K, 4>(x, taps, out, N, C, H, W, stream);
-            case 2: return launch_filter_t<T, K, 2>(x, taps, out, N, C, H, W, stream);
-            default: return launch_filter_t<T, K, 1>(x, taps, out, N, C, H, W, stream);
-        }
-    } else {
-        switch (vec) {
-            case 4: return launch_filter_t<T, K, 4>(x, taps, out, N, C, H, W, stream);
-            case 2: return launch_filter_t<T, K, 2>(x, taps, out, N, C, H, W, stream);
-            default: return launch_filter_t<T, K, 1>(x, taps, out, N, C, H, W, stream);
-        }
+    switch (vec) {
+        case 4: return launch_filter_t<T, K, 4>(x, taps, out, N, C, H, W, stream);
+        case 2: return launch_filter_t<T, K, 2>(x, taps, out, N, C, H, W, stream);
+        default: return launch_filter_t<T, K, 1>(x, taps, out, N, C, H, W, stream);
     }
 }
 
