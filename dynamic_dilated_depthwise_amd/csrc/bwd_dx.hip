@@ -191,9 +191,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
         int b, t, hs, dc;
         bool row_ok;
     };
-    auto shift_of = [&](int s) {
+    // Stages are (combo = b*KK + t, chunk qq), qq fastest; the loop carries both so
+    // no division by the run-time chunk count is needed (K is a constant).
+    auto shift_of = [&](int combo) {
         Shift sh;
-        const int combo = s / nqq;
         sh.b = combo / KK;
         sh.t = combo - sh.b * KK;
         const int D = dilation(sh.b);
@@ -204,19 +205,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
         sh.row_ok = sh.hs >= 0 && sh.hs < H;
         return sh;
     };
-    // y of stage s (shifted segment, one 64-channel chunk) into staging registers
-    auto load_stage = [&](int s, typename S::Regs &R) {
-        const Shift sh = shift_of(s);
-        const int qq = s % nqq;
+    // y of stage (combo, qq) (shifted segment, one 64-channel chunk) into staging registers
+    auto load_stage = [&](int combo, int qq, typename S::Regs &R) {
+        const Shift sh = shift_of(combo);
         const int ws0 = w0 - sh.dc;
         const int64_t rowoff = (int64_t)(sh.row_ok ? sh.hs : 0) * W;
         const bool fast = (kChunk * qq + kChunk <= C) && sh.row_ok && ws0 - (ws0 & 1) >= 0 && ws0 + kSeg <= W;
         S::load(R, yn, kChunk * qq, C, HW, rowoff, ws0, W, sh.row_ok, fast, aligned4);
     };
-    // weight fragments of stage s for this wave's 16 generator rows
-    auto load_A = [&](int s, typename G::AFrag (&a)[S::SUB]) {
-        const Shift sh = shift_of(s);
-        const int qq = s % nqq;
+    // weight fragments of stage (combo, qq) for this wave's 16 generator rows
+    auto load_A = [&](int combo, int qq, typename G::AFrag (&a)[S::SUB]) {
+        const Shift sh = shift_of(combo);
 #pragma unroll
         for (int u = 0; u < S::SUB; ++u) {
             const int q = S::SUB * qq + u;  // MFMA chunk of G::CH input channels
@@ -229,9 +228,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
             }
         }
     };
-    // G_b at the source pixels of the tap of stage s: gs[v][pb] for channel c0+4g+v
-    auto load_G = [&](int s, f32x4 (&gs)[4]) {
-        const Shift sh = shift_of(s);
+    // G_b at the source pixels of tap `combo`: gs[v][pb] for channel c0+4g+v
+    auto load_G = [&](int combo, f32x4 (&gs)[4]) {
+        const Shift sh = shift_of(combo);
         const int ws = w - sh.dc;
         const int odd = sh.dc & 1;
         const bool al_s = aligned4 && ((sh.dc & 3) == 0);
@@ -252,12 +251,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     };
 
     typename S::Regs R;
-    load_stage(0, R);
+    load_stage(0, 0, R);
     S::store(stage[0], R);
     typename G::AFrag acur[S::SUB];
     f32x4 gcur[4], gnext[4];
     if (wave_on) {
-        load_A(0, acur);
+        load_A(0, 0, acur);
         load_G(0, gcur);
     }
     float dacc[4][4];
@@ -268,21 +267,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     f32x4 acc[4];
     __syncthreads();
 
+    int combo = 0, qq = 0;  // current stage
 #pragma unroll 1
     for (int s = 0; s < nstage; ++s) {
         const bool more = s + 1 < nstage;
-        const int qq = s % nqq;
+        const int qn = qq + 1 == nqq ? 0 : qq + 1;  // next stage
+        const int cn = qn == 0 ? combo + 1 : combo;
         typename G::AFrag anext[S::SUB];
         if (more) {
-            load_stage(s + 1, R);
+            load_stage(cn, qn, R);
             if (wave_on) {
-                load_A(s + 1, anext);
-                if ((s + 1) % nqq == 0) load_G(s + 1, gnext);
+                load_A(cn, qn, anext);
+                if (qn == 0) load_G(cn, gnext);
             }
         }
         if (wave_on) {
             if (qq == 0) {
-                const f32x4 bias = *(const f32x4 *)(bl + (s / nqq) * kOutCh + 16 * wave + 4 * g);
+                const f32x4 bias = *(const f32x4 *)(bl + combo * kOutCh + 16 * wave + 4 * g);
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) acc[pb] = bias;
             }
@@ -309,6 +310,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
         }
         if (more) S::store(stage[(s + 1) & 1], R);
         __syncthreads();
+        combo = cn;
+        qq = qn;
     }
 
     if (!wave_on) return;
