@@ -177,14 +177,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     const int nqq = (C + kChunk - 1) / kChunk;
     const int nstage = 3 * KK * nqq;
 
-    __shared__ float bl[3 * KK * kOutCh];  // bl[(b*KK + t)*64 + ch] = bias[(b*C + cg0 + ch)*KK + t]
+    // float32 keeps few registers live (weight fragments one MFMA chunk ahead, G_b
+    // loaded at the start of the stage that uses it: a stage holds 2048 MFMA cycles),
+    // so four workgroups fit a CU; bfloat16 stages are short, so everything a stage
+    // needs is fetched one whole stage ahead.
+    constexpr bool AHEAD = Elem<T>::is_bf16;
     __shared__ __align__(16) T stage[2][S::ELEMS];
-    for (int i = threadIdx.x; i < 3 * KK * kOutCh; i += blockDim.x) {
-        const int combo = i / kOutCh;
-        const int c = cg0 + (i - combo * kOutCh);
-        const int b = combo / KK;
-        const int t = combo - b * KK;
-        bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+    // bfloat16: the biases of this workgroup's channels for every tap, staged once
+    // (bl[(b*KK + t)*64 + ch]); float32 loads a tap's biases with its G_b.
+    __shared__ float bl[AHEAD ? 3 * KK * kOutCh : 1];
+    if constexpr (AHEAD) {
+        for (int i = threadIdx.x; i < 3 * KK * kOutCh; i += blockDim.x) {
+            const int combo = i / kOutCh;
+            const int c = cg0 + (i - combo * kOutCh);
+            const int b = combo / KK;
+            const int t = combo - b * KK;
+            bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+        }
     }
 
     struct Shift {
@@ -213,12 +222,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
         const bool fast = (kChunk * qq + kChunk <= C) && sh.row_ok && ws0 - (ws0 & 1) >= 0 && ws0 + kSeg <= W;
         S::load(R, yn, kChunk * qq, C, HW, rowoff, ws0, W, sh.row_ok, fast, aligned4);
     };
-    // weight fragments of stage (combo, qq) for this wave's 16 generator rows
+    // weight fragment of MFMA chunk u of stage (combo, qq) for this wave's 16 generator rows
+    auto load_A1 = [&](int combo, int qq, int u, typename G::AFrag &a) {
+        const int b = combo / KK;
+        const int t = combo - b * KK;
+        const int q = S::SUB * qq + u;  // MFMA chunk of G::CH input channels
+        if (full && kChunk * qq + kChunk <= C) {
+            a = G::load_A_off(wg + ((int64_t)b * C * KK + t) * C, cA * KK * C + G::CH * q + (G::CH / 4) * g);
+        } else {
+            const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
+            a = G::load_A(arow, q, g, C, cvec);
+        }
+    };
+    // all weight fragments of stage (combo, qq)
     auto load_A = [&](int combo, int qq, typename G::AFrag (&a)[S::SUB]) {
         const Shift sh = shift_of(combo);
 #pragma unroll
         for (int u = 0; u < S::SUB; ++u) {
-            const int q = S::SUB * qq + u;  // MFMA chunk of G::CH input channels
+            const int q = S::SUB * qq + u;
             if (full && kChunk * qq + kChunk <= C) {
                 a[u] = G::load_A_off(wg + ((int64_t)sh.b * C * KK + sh.t) * C, cA * KK * C + G::CH * q +
                                                                                     (G::CH / 4) * g);
@@ -226,6 +247,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
                 const T *arow = cA < C ? wg + ((int64_t)(sh.b * C + cA) * KK + sh.t) * C : nullptr;
                 a[u] = G::load_A(arow, q, g, C, cvec);
             }
+        }
+    };
+    // generator bias of tap `combo` for channels c0+4g+v
+    auto load_bias = [&](int combo, f32x4 &bv) {
+        const int b = combo / KK;
+        const int t = combo - b * KK;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int c = c0 + 4 * g + v;
+            bv[v] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
         }
     };
     // G_b at the source pixels of tap `combo`: gs[v][pb] for channel c0+4g+v
@@ -253,11 +284,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     typename S::Regs R;
     load_stage(0, 0, R);
     S::store(stage[0], R);
-    typename G::AFrag acur[S::SUB];
-    f32x4 gcur[4], gnext[4];
+    typename G::AFrag acur[AHEAD ? S::SUB : 1];
+    f32x4 gcur[4], gnext[4], bcur = f32x4{0.f, 0.f, 0.f, 0.f};
     if (wave_on) {
-        load_A(0, 0, acur);
-        load_G(0, gcur);
+        if constexpr (AHEAD) {
+            load_A(0, 0, acur);
+            load_G(0, gcur);
+        } else {
+            load_A1(0, 0, 0, acur[0]);
+        }
     }
     float dacc[4][4];
 #pragma unroll
@@ -273,39 +308,66 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
         const bool more = s + 1 < nstage;
         const int qn = qq + 1 == nqq ? 0 : qq + 1;  // next stage
         const int cn = qn == 0 ? combo + 1 : combo;
-        typename G::AFrag anext[S::SUB];
+        typename G::AFrag anext[S::SUB];  // bfloat16: the next stage's fragments
         if (more) {
             load_stage(cn, qn, R);
-            if (wave_on) {
-                load_A(cn, qn, anext);
-                if (qn == 0) load_G(cn, gnext);
+            if constexpr (AHEAD) {
+                if (wave_on) {
+                    load_A(cn, qn, anext);
+                    if (qn == 0) load_G(cn, gnext);
+                }
             }
         }
         if (wave_on) {
-            if (qq == 0) {
-                const f32x4 bias = *(const f32x4 *)(bl + combo * kOutCh + 16 * wave + 4 * g);
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) acc[pb] = bias;
-            }
+            const bool last = qq == nqq - 1;  // the tap's last chunk: its G_b term follows
             const T *buf = stage[s & 1];
             const int left = C - kChunk * qq;
             const int nsub = left >= kChunk ? S::SUB : (left + G::CH - 1) / G::CH;
+            if (qq == 0) {
+                // bfloat16: the sum starts at the bias; float32 adds it at the end
+                const f32x4 a0 = AHEAD ? *(const f32x4 *)(bl + combo * kOutCh + 16 * wave + 4 * g)
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < S::SUB; ++u)
-                if (u < nsub) G::mma(acc, acur[u], S::frag(buf, u, g, j));
-            if (qq == nqq - 1) {
+                for (int pb = 0; pb < 4; ++pb) acc[pb] = a0;
+            }
+            if constexpr (AHEAD) {
+#pragma unroll
+                for (int u = 0; u < S::SUB; ++u)
+                    if (u < nsub) G::mma(acc, acur[u], S::frag(buf, u, g, j));
+                if (more) {
+#pragma unroll
+                    for (int u = 0; u < S::SUB; ++u) acur[u] = anext[u];
+                }
+            } else {
+                if (last) {
+                    load_G(combo, gcur);
+                    load_bias(combo, bcur);
+                }
+#pragma unroll
+                for (int u = 0; u < S::SUB; ++u) {
+                    if (u < nsub) {
+                        typename G::AFrag an;
+                        const bool in_stage = u + 1 < nsub;
+                        if (in_stage) load_A1(combo, qq, u + 1, an);
+                        else if (more) load_A1(cn, qn, 0, an);
+                        G::mma(acc, acur[0], S::frag(buf, u, g, j));
+                        if (in_stage || more) acur[0] = an;
+                    }
+                }
+            }
+            if (last) {
+                // the bias is in the fp32 sum before the tap's single rounding
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
 #pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += Elem<T>::quant(acc[pb][v]) * gcur[v][pb];
-                if (more) {
+                    for (int pb = 0; pb < 4; ++pb) {
+                        const float tap = AHEAD ? acc[pb][v] : acc[pb][v] + bcur[v];
+                        dacc[v][pb] += Elem<T>::quant(tap) * gcur[v][pb];
+                    }
+                if (AHEAD && more) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) gcur[v] = gnext[v];
                 }
-            }
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < S::SUB; ++u) acur[u] = anext[u];
             }
         }
         if (more) S::store(stage[(s + 1) & 1], R);
