@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
     constexpr int KK = K * K;
     constexpr bool BF = Elem<T>::is_bf16;
     constexpr int CK = BF ? 32 : 4;  // generator channels per k-step
-    __shared__ f32x4 red[3][MB * 4][64];
+    __shared__ f32x4 red[3][4][64];  // one 16-channel block of the cross-wave sum at a time
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -110,15 +110,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
                 o.a[m] = (c_ok && cp < C) ? wrow[cp] : 0.f;
             }
         };
-        // two items in flight ahead of the MFMAs
-        Ops n1, n2;
+        // the next item's operands are in flight during this item's MFMAs (one item
+        // ahead keeps the kernel at four workgroups per CU)
+        Ops n1;
         if (i0 < i1) fetch(i0, n1);
-        if (i0 + 1 < i1) fetch(i0 + 1, n2);
 #pragma unroll 1
         for (int i = i0; i < i1; ++i) {
             const Ops cur = n1;
-            n1 = n2;
-            if (i + 2 < i1) fetch(i + 2, n2);
+            if (i + 1 < i1) fetch(i + 1, n1);
 #pragma unroll
             for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -195,21 +194,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
         }
     }
 
-    // Fixed-order sum of the four waves' partial products: ((w0 + w1) + w2) + w3.
-    if (wave > 0) {
+    // Fixed-order sum of the four waves' partial products, ((w0 + w1) + w2) + w3, one
+    // 16-channel block at a time through LDS.
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
+    for (int m = 0; m < MB; ++m) {
+        if (wave > 0) {
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) red[wave - 1][m * 4 + pb][lane] = acc[m][pb];
+            for (int pb = 0; pb < 4; ++pb) red[wave - 1][pb][lane] = acc[m][pb];
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc[m][pb] += red[k][pb][lane];
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if (wave != 0) return;
-#pragma unroll 1
-    for (int k = 0; k < 3; ++k)  // one wave's slice at a time keeps the register peak low
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) acc[m][pb] += red[k][m * 4 + pb][lane];
 
     T *__restrict__ yo = gy + (int64_t)n * C * HW;
 #pragma unroll
