@@ -228,7 +228,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
 
 // ============================================================================ dW / db
 // One workgroup = CG generator (branch, tap) pairs x 16 depthwise channels x up to
-// 64 input channels c' of the weight gradient x one token split s.  The kDwWaves waves
+// 64 input channels c' of the weight gradient x one token split s.  With CG = K the
+// pairs are the K taps of one kernel row of one branch: they share G_b, which is
+// then loaded once per chunk.  The kDwWaves waves
 // take interleaved chunks of the split's tokens and are summed in a fixed order
 // through LDS at the end, so each partial element is stored exactly once.
 //   MFMA rows    = channel c0 + i of one (b, t) pair (i = lane%16 as A supplier);
@@ -296,6 +298,7 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
     }
     const int cA = c0 + j;         // A role: depthwise channel
     const bool cA_ok = cA < C;
+    constexpr bool ROWGROUP = CG == K;  // one kernel row of one branch: G_b shared
 
     f32x4 acc[CG][NB];
     float dbacc[CG];
@@ -360,7 +363,8 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
 #pragma unroll
             for (int cc = 0; cc < CG; ++cc) {
                 const int dc = cb_dc[cc];
-                o.gv[cc] = Run<T>::fast(gn + (int64_t)((1 + cb_bl[cc]) * C + cA) * HW + rowoff, w, wal, al, odd);
+                if (!ROWGROUP || cc == 0)
+                    o.gv[cc] = Run<T>::fast(gn + (int64_t)((1 + cb_bl[cc]) * C + cA) * HW + rowoff, w, wal, al, odd);
                 o.xv[cc] = Run<T>::fast(xn + (int64_t)cA * HW + (int64_t)(qh + cb_dr[cc]) * W, w + dc,
                                         wal && (dc % RL == 0), al, ((qw + dc) & 1) != 0);
             }
@@ -383,7 +387,8 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
             for (int cc = 0; cc < CG; ++cc) {
                 const int b = cb_b[cc];
                 if (b >= 0 && cA_ok) {
-                    o.gv[cc] = Run<T>::checked(gn + (int64_t)((1 + b) * C + cA) * HW + rowoff, w, W, true, al);
+                    if (!ROWGROUP || cc == 0)
+                        o.gv[cc] = Run<T>::checked(gn + (int64_t)((1 + b) * C + cA) * HW + rowoff, w, W, true, al);
                     const int hs = qh + cb_dr[cc];
                     const bool hok = hs >= 0 && hs < H;
                     o.xv[cc] = Run<T>::checked(xn + (int64_t)cA * HW + (int64_t)(hok ? hs : 0) * W, w + cb_dc[cc], W,
@@ -418,10 +423,10 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
                         if (b >= 0 && cA_ok) {
                             const int hs = hh + cb_dr[cc];
                             const int ws = ww + cb_dc[cc];
-                            if (hs >= 0 && hs < H && ws >= 0 && ws < W) {
+                            const bool in = hs >= 0 && hs < H && ws >= 0 && ws < W;
+                            if (ROWGROUP ? cc == 0 : in)  // shared G_b: the token's own pixel
                                 o.gv[cc].set_raw(k, gn[(int64_t)((1 + b) * C + cA) * HW + pix]);
-                                o.xv[cc].set_raw(k, xn[(int64_t)cA * HW + (int64_t)hs * W + ws]);
-                            }
+                            if (in) o.xv[cc].set_raw(k, xn[(int64_t)cA * HW + (int64_t)hs * W + ws]);
                         }
                     }
 #pragma unroll
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
         for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
             for (int k = 0; k < RL; ++k) {
-                a[cc][k] = o.gv[cc].at(k) * o.xv[cc].at(k) * cb_valid[cc];
+                a[cc][k] = o.gv[ROWGROUP ? 0 : cc].at(k) * o.xv[cc].at(k) * cb_valid[cc];
                 dbacc[cc] += a[cc][k];
             }
         if constexpr (!BF) {
@@ -542,9 +547,9 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
                                void *gx, void *gy, float *dwp, float *dbp, int S, int N, int C, int H, int W, bool al,
                                hipStream_t stream) {
     const int iA = al ? 1 : 0;
-    // (b, t) pairs per dW workgroup: four pairs share each y run (measured best for
-    // both dtypes at 256x256, C=64).
-    constexpr int CG = 4;
+    // (b, t) pairs per dW workgroup: the K taps of one kernel row (they share G_b and
+    // each y run; measured faster than 2 or 4 consecutive pairs at 256x256, C=64).
+    constexpr int CG = K;
     constexpr int NCOMBO = 3 * K * K;
     // Every grid is checked before the first launch, so a refused call writes nothing.
     const int64_t nblk_dx = bwd_dx_blocks(N, C, H, W);
