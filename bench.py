@@ -84,7 +84,7 @@ KERNEL_SYMBOL = {"filter": "filter_fwd_kernel", "fused_fwd": "fused_fwd_kernel",
 KERNEL_SOURCES = {
     "filter": ["filter_fwd.hip", "common.hpp"],
     "fused_fwd": ["fused_fwd.hip", "gen_mma.hpp", "common.hpp"],
-    "bwd_dx": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
+    "bwd_dx": ["bwd_dx.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dy": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dw": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
     "reduce": ["reduce.hip", "common.hpp"],
