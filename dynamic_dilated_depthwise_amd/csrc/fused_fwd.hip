@@ -24,30 +24,91 @@ constexpr int kTileCols = 64;  // 16 lanes x 4 pixels
 
 template <int K> struct XTile {
     static constexpr int r = (K - 1) / 2;
-    static constexpr int HALO = 5 * r;
+    static constexpr int HALO = 5 * r;                 // rows and columns of halo
+    static constexpr int PADC = (HALO + 3) & ~3;       // left column pad, a multiple of 4
     static constexpr int LH = kTileRows + 2 * HALO;
-    static constexpr int LW = kTileCols + 2 * HALO;
+    static constexpr int LW = kTileCols + 2 * PADC;    // a multiple of 4
     static constexpr int PLANE = LH * LW;
+    static constexpr int NV = 16 * PLANE / 4;          // 4-column runs of the 16-channel tile
     static constexpr int BIAS = 3 * K * K * 16;  // bias of the 16 channels for every (b, t)
     static constexpr size_t bytes = sizeof(float) * (16 * PLANE + BIAS);
 };
 
-// Stage x[n, c0..c0+15, h0-HALO .., w0-HALO ..] into LDS as float, zero outside.
+// Stage x[n, c0..c0+15, h0-HALO .., w0-PADC ..] into LDS as float, zero outside the
+// image and for channels >= C.  `vec`: W % 4 == 0 and 16-byte aligned x, so every
+// 4-column run (w0 and PADC are multiples of 4) lies wholly inside or outside the
+// image and is one vector load.  The trip counts are compile-time constants, so the
+// loads of a batch are all issued before the first LDS store waits for them.
 template <typename T, int K>
 __device__ __forceinline__ void stage_x_tile(float *xs, const T *__restrict__ xn, int c0, int C, int H, int W,
-                                             int64_t HW, int h0, int w0) {
+                                             int64_t HW, int h0, int w0, bool vec) {
     using X = XTile<K>;
-    for (int i = threadIdx.x; i < 16 * X::PLANE; i += blockDim.x) {
-        const int ch = i / X::PLANE;
-        const int rem = i - ch * X::PLANE;
-        const int lr = rem / X::LW;
-        const int lc = rem - lr * X::LW;
-        const int c = c0 + ch;
-        const int hh = h0 - X::HALO + lr;
-        const int ww = w0 - X::HALO + lc;
-        float v = 0.f;
-        if (c < C && hh >= 0 && hh < H && ww >= 0 && ww < W) v = Elem<T>::to_f32(xn[(int64_t)c * HW + (int64_t)hh * W + ww]);
-        xs[i] = v;
+    constexpr int NT = 256;
+    constexpr int VPR = X::LW / 4;
+    if (vec) {
+        constexpr int IT = (X::NV + NT - 1) / NT;
+        constexpr int BATCH = 9;
+#pragma unroll
+        for (int k0 = 0; k0 < IT; k0 += BATCH) {
+            f32x4 v[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                if (k0 + k >= IT) continue;
+                const int i = (k0 + k) * NT + (int)threadIdx.x;
+                const int row = i / VPR;  // channel * LH + lr
+                const int cv = i - row * VPR;
+                const int ch = row / X::LH;
+                const int lr = row - ch * X::LH;
+                const int c = c0 + ch;
+                const int hh = h0 - X::HALO + lr;
+                const int ww = w0 - X::PADC + 4 * cv;
+                const bool ok = i < X::NV && c < C && hh >= 0 && hh < H && ww >= 0 && ww < W;
+                // branch-free: a run outside the image reads the image's first run and is zeroed
+                const T *src = xn + (ok ? (int64_t)c * HW + (int64_t)hh * W + ww : 0);
+                f32x4 t;
+                if constexpr (Elem<T>::is_bf16) {
+                    const u16x4 u = *(const u16x4 *)src;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) t[e] = bf16_bits_to_f32(u[e]);
+                } else {
+                    t = *(const f32x4 *)src;
+                }
+                v[k] = ok ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                const int i = (k0 + k) * NT + (int)threadIdx.x;
+                if (k0 + k < IT && i < X::NV) *(f32x4 *)(xs + 4 * i) = v[k];
+            }
+        }
+    } else {
+        constexpr int NE = 16 * X::PLANE;
+        constexpr int IT = (NE + NT - 1) / NT;
+        constexpr int BATCH = 16;
+#pragma unroll
+        for (int k0 = 0; k0 < IT; k0 += BATCH) {
+            float v[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                if (k0 + k >= IT) continue;
+                const int i = (k0 + k) * NT + (int)threadIdx.x;
+                const int row = i / X::LW;
+                const int lc = i - row * X::LW;
+                const int ch = row / X::LH;
+                const int lr = row - ch * X::LH;
+                const int c = c0 + ch;
+                const int hh = h0 - X::HALO + lr;
+                const int ww = w0 - X::PADC + lc;
+                const bool ok = i < NE && c < C && hh >= 0 && hh < H && ww >= 0 && ww < W;
+                const float e = Elem<T>::to_f32(xn[ok ? (int64_t)c * HW + (int64_t)hh * W + ww : 0]);
+                v[k] = ok ? e : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                const int i = (k0 + k) * NT + (int)threadIdx.x;
+                if (k0 + k < IT && i < NE) xs[i] = v[k];
+            }
+        }
     }
 }
 
@@ -82,10 +143,13 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
 
     const T *__restrict__ xn = x + (int64_t)n * C * HW;
     const T *__restrict__ yn = y + (int64_t)n * C * HW;
-    stage_x_tile<T, K>(xs, xn, c0, C, H, W, HW, h0, w0);
+    stage_x_tile<T, K>(xs, xn, c0, C, H, W, HW, h0, w0, aligned4);
     // bias slice: bl[(b*KK + t)*16 + ch] = bias[(b*C + c0 + ch)*KK + t]
     float *bl = xs + 16 * X::PLANE;
-    for (int i = threadIdx.x; i < X::BIAS; i += blockDim.x) {
+#pragma unroll
+    for (int k = 0; k < (X::BIAS + 255) / 256; ++k) {
+        const int i = k * 256 + (int)threadIdx.x;
+        if (i >= X::BIAS) break;
         const int combo = i >> 4;
         const int c = c0 + (i & 15);
         const int b = combo / KK;
@@ -159,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
             }
             const int ki = t / K;
             const int kj = t - ki * K;
-            const float *xl = xs + (wave + X::HALO + (ki - r) * D) * X::LW + 4 * j + X::HALO + (kj - r) * D;
+            const float *xl = xs + (wave + X::HALO + (ki - r) * D) * X::LW + 4 * j + X::PADC + (kj - r) * D;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const float *xr = xl + (4 * g + v) * X::PLANE;
