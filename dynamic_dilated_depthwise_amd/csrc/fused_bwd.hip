@@ -231,7 +231,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
 // 64 input channels c' of the weight gradient x one token split s.  With CG = K the
 // pairs are the K taps of one kernel row of one branch: they share G_b, which is
 // then loaded once per chunk.  The kDwWaves waves
-// take interleaved chunks of the split's tokens and are summed in a fixed order
+// split the token range (bfloat16: contiguous quarters; float32: interleaved
+// chunks) and are summed in a fixed order
 // through LDS at the end, so each partial element is stored exactly once.
 //   MFMA rows    = channel c0 + i of one (b, t) pair (i = lane%16 as A supplier);
 //   MFMA columns = c' = cn0 + 16*nb + j (j = lane%16 as B supplier);
@@ -309,13 +310,22 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
         for (int nb = 0; nb < NB; ++nb) acc[cc][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // The wave walks chunks of KC tokens (t0 + wave*KC, then every 4*KC), keeping
-    // the chunk's (image, row, column) position incrementally.  A chunk that lies in
-    // one image row loads each operand as one run of RL pixels per lane; a chunk
-    // that crosses a row end or the split end takes the per-token path.
-    int64_t p0 = t0 + (int64_t)wave * KC;
+    // The wave walks chunks of KC tokens of [wl, wh), keeping the chunk's (image,
+    // row, column) position incrementally.  bfloat16: each wave takes a contiguous
+    // quarter of the split, so that consecutive chunks of one wave read the two
+    // halves of the same cache lines (measured faster); float32: the waves take
+    // interleaved chunks (wave, wave + 4, ...) of the whole split (measured faster).
+    // A chunk that lies in one image row loads each operand as one run of RL pixels
+    // per lane; a chunk that crosses a row end or the range end takes the per-token
+    // path.
+    constexpr bool CONTIG = BF;
+    constexpr int STEP = CONTIG ? KC : kDwWaves * KC;  // tokens from one chunk of the wave to its next
+    const int64_t span = t1 - t0;
+    const int64_t wl = CONTIG ? t0 + span * wave / kDwWaves / KC * KC : t0 + (int64_t)wave * KC;
+    const int64_t wh = (!CONTIG || wave + 1 == kDwWaves) ? t1 : t0 + span * (wave + 1) / kDwWaves / KC * KC;
+    int64_t p0 = wl;
     int pn = 0, ph = 0, pw = 0;
-    if (p0 < t1) {
+    if (p0 < wh) {
         pn = (int)(p0 / HW);
         const int64_t rem = p0 - (int64_t)pn * HW;
         ph = (int)(rem / W);
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
         cb_valid[cc] = cb_b[cc] >= 0 ? 1.f : 0.f;
     }
     auto load_chunk = [&](int64_t q0, int qn, int qh, int qw, Raw &o) {
-        const bool in_row = (q0 + KC <= t1) && (qw + KC <= W);
+        const bool in_row = (q0 + KC <= wh) && (qw + KC <= W);
         // Wave-uniform: the whole chunk is one row segment, every channel exists and
         // every shifted run lies inside its row -> one straight-line block of loads.
         bool fast = in_row && chfull && cpfull;
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
             }
 #pragma unroll
             for (int k = 0; k < RL; ++k) {
-                if (pf + k < t1) {
+                if (pf + k < wh) {
                     const T *xn = x + (int64_t)nn * CHW;
                     const T *gn = gout + (int64_t)nn * 4 * CHW;
                     const T *yn = y + (int64_t)nn * CHW;
@@ -446,8 +456,8 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
         }
     };
     auto advance = [&](int64_t &q0, int &qn, int &qh, int &qw) {
-        q0 += kDwWaves * KC;
-        qw += kDwWaves * KC;
+        q0 += STEP;
+        qw += STEP;
         while (qw >= W) {
             qw -= W;
             if (++qh == H) {
@@ -492,11 +502,11 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
     // The next chunk's loads are issued before this chunk's products and MFMAs.
     {
         Raw nxt;
-        if (p0 < t1) load_chunk(p0, pn, ph, pw, nxt);
-        while (p0 < t1) {
+        if (p0 < wh) load_chunk(p0, pn, ph, pw, nxt);
+        while (p0 < wh) {
             const Raw cur = nxt;
             advance(p0, pn, ph, pw);
-            if (p0 < t1) load_chunk(p0, pn, ph, pw, nxt);
+            if (p0 < wh) load_chunk(p0, pn, ph, pw, nxt);
             consume(cur);
         }
     }
