@@ -112,6 +112,26 @@ __device__ __forceinline__ void stage_x_tile(float *xs, const T *__restrict__ xn
     }
 }
 
+// Store four values that were widened exactly from T (float, or bf16 bits << 16)
+// back as their original bits: the x block of the output is a bit-exact copy.
+template <typename T>
+__device__ __forceinline__ void store4_bits(T *__restrict__ row, int w, int W, f32x4 v, bool aligned4) {
+    if (w + 3 < W && aligned4) {
+        if constexpr (Elem<T>::is_bf16) {
+            u16x4 u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) u[k] = exact_narrow<T>(v[k]);
+            *(u16x4 *)(row + w) = u;
+        } else {
+            *(f32x4 *)(row + w) = v;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (w + k < W) row[w + k] = exact_narrow<T>(v[k]);
+    }
+}
+
 template <typename T, int K, int KQ>
 __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__ x, const T *__restrict__ y,
                                                            const T *__restrict__ wg, const T *__restrict__ bg,
@@ -169,6 +189,29 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
         for (int q = 0; q < KQ; ++q) bres[q] = G::load_B(yn, q, g, C, HW, rowoff, w, W, row_ok, aligned4);
     }
     __syncthreads();
+
+    // Outputs are stored as soon as they are final, so that the stores overlap the
+    // remaining taps: the x block now, from the staged tile (its interior holds the
+    // row's 64 pixels of the 16 channels), and each branch after its last tap.
+    T *__restrict__ on = out + (int64_t)n * 4 * C * HW;
+    auto store_branch = [&](int b, const float (&ob)[4][4]) {
+        if (!row_ok) return;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int c = c0 + 4 * g + v;
+            if (c < C)
+                store4_row(on + (int64_t)((1 + b) * C + c) * HW + rowoff, w, W,
+                           f32x4{ob[v][0], ob[v][1], ob[v][2], ob[v][3]}, aligned4);
+        }
+    };
+    if (row_ok) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int c = c0 + 4 * g + v;
+            const f32x4 xv = *(const f32x4 *)(xs + (4 * g + v) * X::PLANE + (wave + X::HALO) * X::LW + X::PADC + 4 * j);
+            if (c < C) store4_bits(on + (int64_t)c * HW + rowoff, w, W, xv, aligned4);
+        }
+    }
 
     const int cA = c0 + j;  // channel of the generator row this lane supplies
     // Wave-uniform: all 16 channels exist, every weight chunk is whole and vector-aligned.
@@ -231,19 +274,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
                 for (int pb = 0; pb < 4; ++pb) oacc[b][v][pb] += Elem<T>::quant(acc[pb][v]) * xr[pb];
             }
         }
-    }
-
-    if (!row_ok) return;
-    T *__restrict__ on = out + (int64_t)n * 4 * C * HW;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int c = c0 + 4 * g + v;
-        if (c >= C) continue;
-        copy4_row(xn + (int64_t)c * HW + rowoff, on + (int64_t)c * HW + rowoff, w, W, aligned4);
-#pragma unroll
-        for (int b = 0; b < 3; ++b)
-            store4_row(on + (int64_t)((1 + b) * C + c) * HW + rowoff, w, W,
-                       f32x4{oacc[b][v][0], oacc[b][v][1], oacc[b][v][2], oacc[b][v][3]}, aligned4);
+        store_branch(b, oacc[b]);
     }
 }
 
