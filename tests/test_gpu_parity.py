@@ -251,3 +251,42 @@ def test_finite_difference_spot_check():
         # |fd - an| far below 2e-5 of it, while a wrong or missing term does not.
         scale = float(np.linalg.norm(gv) * np.linalg.norm(vv))
         assert abs(fd - an) <= 2e-5 * scale + 5e-3, f"FD {name}: {fd} vs {an} (scale {scale:.3g})"
+
+
+# Special values in x: the x block of both forward outputs is a copy of x, so every
+# bit pattern must come through unchanged (signed zeros, infinities, NaNs with
+# payloads and the sign bit set, subnormals), whatever the other blocks hold.
+_SPECIAL_F32 = [0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00001, 0xFFA5A5A5, 0x7F800001,
+                0x00000001, 0x807FFFFF, 0x3F800000]
+_SPECIAL_BF16 = [0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC1, 0xFFA5, 0x7F81, 0x0001, 0x807F, 0x3F80]
+
+
+def _with_specials(x, dt, seed):
+    g = torch.Generator().manual_seed(seed)
+    n = x.numel()
+    pos = torch.randperm(n, generator=g)[: max(1, n // 7)]
+    if dt == torch.float32:
+        bits = x.view(torch.int32).reshape(-1).clone()
+        pat = torch.tensor(_SPECIAL_F32, dtype=torch.int64).to(torch.int32)
+    else:
+        bits = x.view(torch.int16).reshape(-1).clone()
+        pat = torch.tensor(_SPECIAL_BF16, dtype=torch.int64).to(torch.int16)
+    bits[pos] = pat[torch.arange(pos.numel()) % pat.numel()]
+    return bits.view(x.dtype).reshape(x.shape)
+
+
+@pytest.mark.parametrize("path", ["filter", "fused"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [S_(2, 24, 15, 17, 3), S_(1, 64, 9, 130, 5), S_(1, 16, 6, 64, 1)],
+                         ids=["nonaligned_k3", "c64_w130_k5", "w64_k1"])
+def test_x_block_bit_exact_specials(shape, dt, path):
+    dtype = DT[dt]
+    h = inputs(shape, 301, dtype, taps=(path == "filter"))
+    h["x"] = _with_specials(h["x"], dtype, 302)
+    d = dev(h)
+    announce("x block specials", path, dt, shape)
+    out = gpu_filter(d, shape.K) if path == "filter" else gpu_fused(d, shape.K)
+    ibits = torch.int32 if dtype == torch.float32 else torch.int16
+    got = out[:, : shape.C].contiguous().cpu().view(ibits)
+    want = h["x"].contiguous().view(ibits)
+    assert torch.equal(got, want), f"x block differs in {int((got != want).sum())} elements"
