@@ -90,13 +90,14 @@ def test_training(name, shape, seed, dt, path):
 
 
 def test_auto_and_mismatch_paths():
-    """Automatic mode follows the measured thresholds (bf16 K=3 trains fused at any
-    size, fp32 K=3 below 128^2 materialised); a dtype mismatch takes the
+    """Automatic mode follows the measured thresholds (bf16 K=3 trains fused from
+    1024 tokens, fp32 K=3 below 128^2 materialised); a dtype mismatch takes the
     materialised path and computes in the generator's dtype."""
     shape, seed = S_(1, 16, 10, 12, 3), 405
-    mb = _module(shape, torch.bfloat16, seed)
-    hb = synth.make_inputs(shape, seed, torch.bfloat16)
-    announce("module auto/mismatch", shape)
+    sb = S_(1, 16, 32, 40, 3)  # 1280 tokens
+    mb = _module(sb, torch.bfloat16, seed)
+    hb = synth.make_inputs(sb, seed, torch.bfloat16)
+    announce("module auto/mismatch", shape, sb)
     mb(hb["x"].cuda().requires_grad_(True), hb["y"].cuda())
     assert mb.last_path == "fused"
     m = _module(shape, torch.float32, seed)

@@ -13,7 +13,7 @@ def test_thresholds_table():
             for K in (3, 5):
                 assert (mode, dt, K) in AUTO_MIN_TOKENS
     assert auto_min_tokens(True, F32, 1) == auto_min_tokens(True, F32, 3)
-    assert auto_min_tokens(True, BF16, 5) is None  # measured: never faster fused
+    assert auto_min_tokens(True, BF16, 5) == 65536  # measured: fused faster only from 256^2
 
 
 def test_inference_path():
@@ -31,8 +31,10 @@ def test_training_path():
     big = 1 << 20
     assert choose_path(True, big, 3, F32, F32, F32, False) == "fused"
     assert choose_path(True, 100, 3, F32, F32, F32, False) == "materialised"
-    assert choose_path(True, 100, 3, BF16, BF16, BF16, False) == "fused"
-    assert choose_path(True, big, 5, BF16, BF16, BF16, False) == "materialised"
+    assert choose_path(True, 100, 3, BF16, BF16, BF16, False) == "materialised"
+    assert choose_path(True, 2048, 3, BF16, BF16, BF16, False) == "fused"
+    assert choose_path(True, 36864, 5, BF16, BF16, BF16, False) == "materialised"
+    assert choose_path(True, big, 5, BF16, BF16, BF16, False) == "fused"
     assert choose_path(True, big, 3, F32, F32, F32, True) == "materialised"           # autocast
     assert choose_path(True, big, 3, F32, F32, BF16, False) == "materialised"         # dtype mismatch
     assert choose_path(True, big, 3, F32, F32, F32, False, fused_training=False) == "materialised"
