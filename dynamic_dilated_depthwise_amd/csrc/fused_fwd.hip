@@ -14,6 +14,8 @@
 //   x tile with its 5*(K-1)/2 halo.  The three branch sums stay in registers.
 // y is read once per wave into registers (the MFMA B operand is the same for
 // all 3*K*K generator blocks) when C <= 64; larger C streams it per block.
+#include <algorithm>
+
 #include "gen_mma.hpp"
 #include "launchers.hpp"
 
@@ -21,6 +23,7 @@ namespace ddpm {
 
 constexpr int kTileRows = 4;   // one row per wave
 constexpr int kTileCols = 64;  // 16 lanes x 4 pixels
+constexpr int kCUs = 256;        // compute units of the chip (MI355X)
 
 template <int K> struct XTile {
     static constexpr int r = (K - 1) / 2;
@@ -135,7 +138,8 @@ __device__ __forceinline__ void store4_bits(T *__restrict__ row, int w, int W, f
 template <typename T, int K, int KQ>
 __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__ x, const T *__restrict__ y,
                                                            const T *__restrict__ wg, const T *__restrict__ bg,
-                                                           T *__restrict__ out, int C, int H, int W, int al) {
+                                                           T *__restrict__ out, int C, int H, int W, int al,
+                                                           int split) {
     using G = Gen<T>;
     using X = XTile<K>;
     constexpr int r = X::r;
@@ -147,10 +151,14 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nCB = (C + 15) >> 4;
-    // logical tile order: channel block fastest, then column tile, row band, image
+    // logical tile order: (branch when split,) channel block, column tile, row band,
+    // image.  split = 3: each workgroup computes one dilation branch of its tile (the
+    // three write separate output blocks), for grids too small to fill the chip.
     const int ncolt = (W + kTileCols - 1) / kTileCols;
     const int nbands = (H + kTileRows - 1) / kTileRows;
     int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bsel = split == 3 ? L % 3 : -1;  // the branch this workgroup computes, -1: all
+    if (split == 3) L /= 3;
     const int c0 = (L % nCB) * 16;
     L /= nCB;
     const int w0 = (L % ncolt) * kTileCols;
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
                            f32x4{ob[v][0], ob[v][1], ob[v][2], ob[v][3]}, aligned4);
         }
     };
-    if (row_ok) {
+    if (row_ok && bsel <= 0) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int c = c0 + 4 * g + v;
@@ -228,6 +236,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const int aoff = cA * KK * C + 4 * (Elem<T>::is_bf16 ? 2 : 1) * g;  // lane's offset inside a (b, t) slice
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
+        if (bsel >= 0 && b != bsel) continue;  // wave-uniform
         const int D = dilation(b);
         // Generator-row operand of tap t of this branch.
         auto fetch = [&](int t, typename G::AFrag (&af)[KQ > 0 ? KQ : 1]) {
@@ -290,8 +299,13 @@ static hipError_t launch_fused_t(const void *x, const void *y, const void *wg, c
     const int64_t nblk = (int64_t)((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows) * N *
                          ((C + 15) / 16);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), lds, stream, (const T *)x, (const T *)y, (const T *)wg,
-                       (const T *)bg, (T *)out, C, H, W, al ? 1 : 0);
+    // When one workgroup per (tile, branch) still fits the chip in one round (256 CUs,
+    // each holding as many of these workgroups as its 160 KB of LDS allows, at most
+    // two), split the branches: each workgroup then does a third of the serial taps.
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, (int64_t)(160 * 1024) / (int64_t)lds));
+    const int split = nblk * 3 <= kCUs * per_cu ? 3 : 1;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(nblk * split)), dim3(256), lds, stream, (const T *)x, (const T *)y,
+                       (const T *)wg, (const T *)bg, (T *)out, C, H, W, al ? 1 : 0, split);
     return hipGetLastError();
 }
 

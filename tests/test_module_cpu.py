@@ -19,7 +19,8 @@ def test_thresholds_table():
 def test_inference_path():
     assert choose_path(False, 10, 3, F32, F32, F32, False) == "fused"
     assert choose_path(False, 10, 5, BF16, BF16, BF16, False) == "fused"
-    assert choose_path(False, 10, 5, F32, F32, F32, False) == "materialised"          # below the fp32 K=5 limit
+    assert choose_path(False, 10, 5, F32, F32, F32, False) == "fused"
+    assert choose_path(False, 10, 5, F32, F32, F32, False, min_tokens=11) == "materialised"
     assert choose_path(False, 10, 5, F32, F32, F32, False, fused_inference=True) == "fused"
     assert choose_path(False, 10, 3, F32, F32, F32, False, fused_inference=False) == "materialised"
     assert choose_path(False, 10, 3, F32, F32, F32, True) == "materialised"           # autocast
