@@ -13,7 +13,7 @@ One step is one pass of the whole hot path over one batch of synthetic input
   6. ddpm_reduce_partials  fixed-order sum of the partials
 The backward of the materialised filter (ddpm_filter_bwd: dX and the tap
 gradient) is timed the same way right after the steps, outside ms_per_step.
-Each library call runs one kernel (the reduce runs two short ones), so HIP events
+Each library call runs one kernel, so HIP events
 recorded around every call on the launch stream give per-kernel durations over
 the timed region.  All inputs are resident in HBM before timing starts.
 

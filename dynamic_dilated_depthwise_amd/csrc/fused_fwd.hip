@@ -135,11 +135,10 @@ __device__ __forceinline__ void store4_bits(T *__restrict__ row, int w, int W, f
     }
 }
 
-template <typename T, int K, int KQ>
+template <typename T, int K, int KQ, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__ x, const T *__restrict__ y,
                                                            const T *__restrict__ wg, const T *__restrict__ bg,
-                                                           T *__restrict__ out, int C, int H, int W, int al,
-                                                           int split) {
+                                                           T *__restrict__ out, int C, int H, int W, int al) {
     using G = Gen<T>;
     using X = XTile<K>;
     constexpr int r = X::r;
@@ -151,14 +150,14 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nCB = (C + 15) >> 4;
-    // logical tile order: (branch when split,) channel block, column tile, row band,
-    // image.  split = 3: each workgroup computes one dilation branch of its tile (the
+    // logical tile order: (branch when SPLIT,) channel block, column tile, row band,
+    // image.  SPLIT: each workgroup computes one dilation branch of its tile (the
     // three write separate output blocks), for grids too small to fill the chip.
     const int ncolt = (W + kTileCols - 1) / kTileCols;
     const int nbands = (H + kTileRows - 1) / kTileRows;
     int L = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int bsel = split == 3 ? L % 3 : -1;  // the branch this workgroup computes, -1: all
-    if (split == 3) L /= 3;
+    const int bsel = SPLIT ? L % 3 : -1;  // the branch this workgroup computes, -1: all
+    if (SPLIT) L /= 3;
     const int c0 = (L % nCB) * 16;
     L /= nCB;
     const int w0 = (L % ncolt) * kTileCols;
@@ -212,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
                            f32x4{ob[v][0], ob[v][1], ob[v][2], ob[v][3]}, aligned4);
         }
     };
-    if (row_ok && bsel <= 0) {
+    if (row_ok && (!SPLIT || bsel == 0)) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int c = c0 + 4 * g + v;
@@ -236,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const int aoff = cA * KK * C + 4 * (Elem<T>::is_bf16 ? 2 : 1) * g;  // lane's offset inside a (b, t) slice
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
-        if (bsel >= 0 && b != bsel) continue;  // wave-uniform
+        if (SPLIT && b != bsel) continue;  // wave-uniform
         const int D = dilation(b);
         // Generator-row operand of tap t of this branch.
         auto fetch = [&](int t, typename G::AFrag (&af)[KQ > 0 ? KQ : 1]) {
@@ -290,10 +289,13 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
 template <typename T, int K, int KQ>
 static hipError_t launch_fused_t(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
                                  int C, int H, int W, bool al, hipStream_t stream) {
-    auto kern = fused_fwd_kernel<T, K, KQ>;
+    auto kern = fused_fwd_kernel<T, K, KQ, false>;
+    auto kern_split = fused_fwd_kernel<T, K, KQ, true>;
     const size_t lds = XTile<K>::bytes;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)kern_split, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int64_t nblk = (int64_t)((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows) * N *
@@ -303,9 +305,12 @@ static hipError_t launch_fused_t(const void *x, const void *y, const void *wg, c
     // each holding as many of these workgroups as its 160 KB of LDS allows, at most
     // two), split the branches: each workgroup then does a third of the serial taps.
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, (int64_t)(160 * 1024) / (int64_t)lds));
-    const int split = nblk * 3 <= kCUs * per_cu ? 3 : 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(nblk * split)), dim3(256), lds, stream, (const T *)x, (const T *)y,
-                       (const T *)wg, (const T *)bg, (T *)out, C, H, W, al ? 1 : 0, split);
+    if (nblk * 3 <= kCUs * per_cu)
+        hipLaunchKernelGGL(kern_split, dim3((unsigned)(nblk * 3)), dim3(256), lds, stream, (const T *)x, (const T *)y,
+                           (const T *)wg, (const T *)bg, (T *)out, C, H, W, al ? 1 : 0);
+    else
+        hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), lds, stream, (const T *)x, (const T *)y,
+                           (const T *)wg, (const T *)bg, (T *)out, C, H, W, al ? 1 : 0);
     return hipGetLastError();
 }
 
