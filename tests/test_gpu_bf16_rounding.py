@@ -1,0 +1,122 @@
+"""bf16 tap quantisation, checked bit for bit on the GPU.
+
+The page quantises the taps to bfloat16 before they are used ("CUDA Flash 式融合训练",
+precision paragraph); the reading taken here rounds each tap once, round to nearest
+even, after the fp32 generator sum plus bias, and rounds every bf16 output once.
+With K = 1 and one channel every step is either exact in fp32 (a product of two
+bf16 values) or one fp32 addition in a fixed order, so a few lines of numpy with an
+explicit bf16 rounding predict the kernels' outputs exactly:
+  fused forward   out_b = rne(rne(W_b y + b_b) x)
+  fused dX        dX = rne(((0 + q_0 G_0) + q_1 G_1) + q_2 G_2 + G_x),  q_b = rne(W_b y + b_b)
+The same model without the tap rounding must differ somewhere, so the test tells the
+two readings apart.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_dilated_depthwise_amd as ddpm
+
+pytestmark = pytest.mark.gpu
+
+
+def _rne_bits(a):
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _bits_f32(b):
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _rne(a):
+    return _bits_f32(_rne_bits(a))
+
+
+def _draw(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+def _case(seed):
+    H, W = 9, 70
+    x = _draw((1, 1, H, W), seed)
+    y = _draw((1, 1, H, W), seed + 1)
+    w = _draw((3, 1), seed + 2)
+    b = _draw((3,), seed + 3, 0.3)
+    gout = _draw((1, 4, H, W), seed + 4)
+    f = lambda t: t.float().numpy()
+    return x, y, w, b, gout, f(x)[0, 0], f(y)[0, 0], f(w)[:, 0], f(b), f(gout)[0]
+
+
+def _taps(yv, wv, bv, quantise):
+    T = [np.float32(wv[k]) * yv + np.float32(bv[k]) for k in range(3)]  # product exact, one rounding
+    T = [t.astype(np.float32) for t in T]
+    return [_rne(t) for t in T] if quantise else T
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_fused_forward_rounds_taps(seed):
+    x, y, w, b, _, xv, yv, wv, bv, _ = _case(seed)
+    out = torch.empty((1, 4, *x.shape[2:]), device="cuda", dtype=torch.bfloat16)
+    ddpm.ddpm_fused_fwd(x.cuda(), y.cuda(), w.cuda(), b.cuda(), out, 1)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = [_rne_bits((q * xv).astype(np.float32)) for q in _taps(yv, wv, bv, True)]
+    plain = [_rne_bits((t * xv).astype(np.float32)) for t in _taps(yv, wv, bv, False)]
+    for k in range(3):
+        assert np.array_equal(got[0, 1 + k], want[k]), f"branch {k}: not rne(rne(T) x)"
+    assert any(not np.array_equal(want[k], plain[k]) for k in range(3)), "case does not separate the readings"
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_fused_dx_rounds_taps(seed):
+    x, y, w, b, gout, xv, yv, wv, bv, gv = _case(seed)
+    gx = torch.empty_like(x, device="cuda")
+    ddpm.ddpm_fused_bwd(x.cuda(), y.cuda(), w.cuda(), b.cuda(), gout.cuda(), gx, None, None, None, 1)
+    torch.cuda.synchronize()
+    got = gx.cpu().view(torch.int16).numpy().view(np.uint16)[0, 0]
+
+    def model(quantise):
+        q = _taps(yv, wv, bv, quantise)
+        acc = np.zeros_like(xv, dtype=np.float32)
+        for k in range(3):
+            acc = (acc + (q[k] * gv[1 + k]).astype(np.float32)).astype(np.float32)
+        return _rne_bits((acc + gv[0]).astype(np.float32))
+
+    assert np.array_equal(got, model(True)), "dX is not the sum of rounded taps times G"
+    assert not np.array_equal(model(True), model(False)), "case does not separate the readings"
+
+
+def _grid_values(shape, seed):
+    """bf16 values 1 + k/128, k in 0..3: products and sums of a few dozen of them are
+    exact in fp32 whatever the summation order."""
+    g = torch.Generator().manual_seed(seed)
+    k = torch.randint(0, 4, shape, generator=g).float()
+    return (1.0 + k / 128.0).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_weight_gradient_rounds_dk_bias_gradient_does_not(seed):
+    """dW sums rne(dK) * y (dK is a bf16 MFMA operand), db sums the fp32 dK unrounded;
+    with K = 1, dK_b = G_b * x at the same pixel."""
+    H, W = 4, 6
+    x = _grid_values((1, 1, H, W), seed)
+    y = _grid_values((1, 1, H, W), seed + 1)
+    gout = _grid_values((1, 4, H, W), seed + 2)
+    w = _draw((3, 1), seed + 3)
+    b = _draw((3,), seed + 4, 0.3)
+    pw = torch.empty((1, 3, 1), device="cuda", dtype=torch.float32)
+    pb = torch.empty((1, 3), device="cuda", dtype=torch.float32)
+    ddpm.ddpm_fused_bwd(x.cuda(), y.cuda(), w.cuda(), b.cuda(), gout.cuda(), None, None, pw, pb, 1)
+    torch.cuda.synchronize()
+    xv, yv, gv = x.float().numpy()[0, 0], y.float().numpy()[0, 0], gout.float().numpy()[0]
+    for k in range(3):
+        dk = (gv[1 + k] * xv).astype(np.float32)  # exact
+        want_w = np.float32(np.sum(_rne(dk).astype(np.float64) * yv))  # every partial sum exact
+        want_b = np.float32(np.sum(dk.astype(np.float64)))
+        other_w = np.float32(np.sum(dk.astype(np.float64) * yv))
+        other_b = np.float32(np.sum(_rne(dk).astype(np.float64)))
+        assert pw[0, k, 0].item() == want_w, f"dW row {k}: {pw[0, k, 0].item()!r} != {want_w!r}"
+        assert pb[0, k].item() == want_b, f"db row {k}: {pb[0, k].item()!r} != {want_b!r}"
+        assert want_w != other_w and want_b != other_b, "case does not separate the readings"
