@@ -472,7 +472,9 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
         for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
             for (int k = 0; k < RL; ++k) {
-                a[cc][k] = o.gv[ROWGROUP ? 0 : cc].at(k) * o.xv[cc].at(k) * cb_valid[cc];
+                // (when CG divides the pair count every slot is a real pair: no mask)
+                a[cc][k] = o.gv[ROWGROUP ? 0 : cc].at(k) * o.xv[cc].at(k);
+                if constexpr (NCOMBO % CG != 0) a[cc][k] *= cb_valid[cc];
                 dbacc[cc] += a[cc][k];
             }
         if constexpr (!BF) {
