@@ -39,6 +39,8 @@ FWD_CASES = [
     ("c48_ragged", (S_(1, 48, 12, 70, 3), 113)), ("c64_w200_k5", (S_(1, 64, 9, 200, 5), 114)),
     # rows wider than one tile (several column tiles; the checked backward dX path)
     ("w520_wide", (S_(1, 4, 6, 520, 3), 115)), ("w1030_k5", (S_(1, 3, 5, 1030, 5), 116)),
+    # a batch of four mid-size images on the workload's channel count (full-size grids)
+    ("batch4_c64_64", (S_(4, 64, 64, 64, 3), 117)),
 ]
 
 BWD_CASES = [
@@ -49,6 +51,7 @@ BWD_CASES = [
     ("ragged_tiles", (S_(3, 16, 9, 65, 3), 208)), ("c33", (S_(1, 33, 10, 8, 3), 209)),
     ("c70_streamed", (S_(1, 70, 12, 20, 3), 210)), ("c2_k5_tall", (S_(2, 2, 37, 6, 5), 212)),
     ("c48_ragged", (S_(1, 48, 12, 70, 3), 213)), ("c64_w200_k5", (S_(1, 64, 9, 200, 5), 214)),
+    ("batch4_c64_64", (S_(4, 64, 64, 64, 3), 215)),
 ]
 
 
