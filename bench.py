@@ -180,7 +180,7 @@ def main():
     shape, block = synth.WORKLOADS[args.workload]
     N, C, H, W, K = shape.N, shape.C, shape.H, shape.W, shape.K
     R = shape.R
-    S = ddpm.num_partials_for(N, H, W)
+    S = ddpm.num_partials_for(N, C, H, W, K)
     log(f"workload {args.workload} N={N} C={C} H={H} W={W} K={K} dtype={args.dtype} S={S}")
 
     h = synth.make_inputs(shape, block, dtype, taps=True, grad=True)

@@ -274,8 +274,12 @@ __global__ __launch_bounds__(64 * kDwWaves) void bwd_dw_kernel(const T *__restri
     const int64_t HW = (int64_t)H * W;
     const int64_t CHW = (int64_t)C * HW;
     const int64_t ntok = (int64_t)N * HW;
-    const int64_t t0 = ntok * s / S;
-    const int64_t t1 = ntok * (s + 1) / S;
+    // Split s covers [t0, t1): the even cut ntok*s/S rounded down to a whole round
+    // of the four waves' chunks, so that every chunk starts on a chunk boundary
+    // (the last split ends at ntok).
+    constexpr int64_t ROUND = (int64_t)kDwWaves * 4 * Run<T>::RL;
+    const int64_t t0 = ntok * s / S / ROUND * ROUND;
+    const int64_t t1 = s + 1 == S ? ntok : ntok * (s + 1) / S / ROUND * ROUND;
     const int64_t R = 3LL * C * KK;
 
     // Per combo: branch, row/column shift; invalid combos get b = -1.

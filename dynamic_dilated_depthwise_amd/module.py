@@ -95,7 +95,7 @@ class DDPMFused(torch.autograd.Function):
         gw = gb = None
         pw = pb = None
         if need_w or need_b:
-            S = num_partials_for(N, H, W)
+            S = num_partials_for(N, C, H, W, K)
             pw = torch.empty((S, R, C), device=x.device, dtype=torch.float32)
             pb = torch.empty((S, R), device=x.device, dtype=torch.float32)
         if gx is not None or gy is not None or pw is not None:

@@ -135,10 +135,13 @@ int ddpm_fused_fwd(const void *x, const void *y, const void *weight, const void 
  *   grad_y   [N, C, H, W]             out  dtype
  *   dweight_partials [num_partials, 3*C*K*K, C]   out  float32
  *   dbias_partials   [num_partials, 3*C*K*K]      out  float32
- *   num_partials in [1, DDPM_MAX_PARTIALS]: the N*H*W tokens, in (n, h, w)
- *   order, are cut into num_partials contiguous ranges whose lengths differ by
- *   at most one; partial s holds the sum over range s.  Reduce them with
- *   ddpm_reduce_partials.
+ *   num_partials in [1, DDPM_MAX_PARTIALS]: the T = N*H*W tokens, in (n, h, w)
+ *   order, are cut into num_partials contiguous ranges; range s starts at
+ *   floor(T*s/num_partials) rounded down to a multiple of 64 tokens (float32) or
+ *   128 tokens (bfloat16), the last ends at T (a range may be empty; its partial
+ *   is zero); partial s holds the sum over range s.  Reduce them with
+ *   ddpm_reduce_partials.  Which count is fastest depends on the grid; the
+ *   Python binding's num_partials_for picks one.
  *   Optional outputs: grad_x may be NULL (dX is not computed), grad_y may be
  *   NULL (dY is not computed), and dweight_partials / dbias_partials may both be
  *   NULL (dWeight / dbias are not computed; then num_partials is ignored).  At

@@ -85,7 +85,7 @@ def gpu_bwd(d, K, S=None):
     x = d["x"]
     N, C, H, W = x.shape
     R = 3 * C * K * K
-    S = ddpm.num_partials_for(N, H, W) if S is None else S
+    S = ddpm.num_partials_for(N, C, H, W, K) if S is None else S
     gx = torch.empty_like(x)
     gy = torch.empty_like(x)
     pw = torch.empty((S, R, C), device="cuda", dtype=torch.float32)

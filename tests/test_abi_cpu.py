@@ -148,8 +148,17 @@ def test_binding_rejects_host_tensors():
 
 
 def test_num_partials_policy():
-    assert ddpm.num_partials_for(1, 16, 16) == 1
-    assert ddpm.num_partials_for(2, 15, 17) == 1
-    assert ddpm.num_partials_for(1, 128, 128) == 16
-    assert ddpm.num_partials_for(1, 256, 256) == 16
-    assert ddpm.num_partials_for(1, 40, 40) == 2
+    # small inputs: one split per 1024 tokens
+    assert ddpm.num_partials_for(1, 8, 16, 16, 3) == 1
+    assert ddpm.num_partials_for(2, 24, 15, 17, 3) == 1
+    assert ddpm.num_partials_for(1, 64, 40, 40, 3) == 2
+    # K = 3, C = 64: 36 workgroups per split; 14 splits keep every CU at two or fewer
+    assert ddpm.num_partials_for(1, 64, 128, 128, 3) == 14
+    assert ddpm.num_partials_for(1, 64, 256, 256, 3) == 14
+    # K = 5, C = 64: 60 per split; every count up to 16 leaves the busiest CU a quarter
+    # of a split's worth, and the tie goes to 16
+    assert ddpm.num_partials_for(1, 64, 128, 128, 5) == 16
+    # K = 1: 12 per split, 16 splits fit in one round
+    assert ddpm.num_partials_for(1, 64, 256, 256, 1) == 16
+    for args in [(1, 64, 256, 256, 3), (4, 1024, 64, 64, 5), (1, 1, 1, 1, 1), (3, 33, 99, 101, 5)]:
+        assert 1 <= ddpm.num_partials_for(*args) <= ddpm.MAX_PARTIALS

@@ -28,7 +28,7 @@ def test_graph_replays_match_eager(name, shape, dt):
     d = dev(inputs(shape, 501, dtype, taps=True, grad=True))
     N, C, H, W = d["x"].shape
     R = 3 * C * K * K
-    S = ddpm.num_partials_for(N, H, W)
+    S = ddpm.num_partials_for(N, C, H, W, K)
     outs = {
         "filter": torch.empty((N, 4 * C, H, W), device="cuda", dtype=dtype),
         "filter_gx": torch.empty_like(d["x"]),
