@@ -17,6 +17,7 @@
 namespace ddpm {
 
 constexpr int kRows = 4;   // one row per wave
+constexpr int kCUs = 256;  // compute units of the chip (MI355X)
 constexpr int kCols = 64;  // 16 lanes x 4 pixels
 
 // ============================================================================ dY
@@ -27,18 +28,22 @@ constexpr int kCols = 64;  // 16 lanes x 4 pixels
 //   float32: one k-step = 4 generator rows (b, 4cq + g, t), lane group g;
 //   bfloat16: one k-step = 32 generator rows (b, 32cq + 8g + e, t); dK is rounded
 //   to bfloat16 as the MFMA operand.
-// The contraction items (channel chunk cq, branch b, tap t) are split into four
-// contiguous ranges, one per wave, and the four partial products are summed in a
+// The contraction items (channel chunk cq, branch b, tap t) are split into NW
+// contiguous ranges, one per wave, and the NW partial products are summed in a
 // fixed order through LDS, so one workgroup per row segment still fills the chip.
-template <typename T, int K, int MB>
-__global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x, const T *__restrict__ wg,
-                                                        const T *__restrict__ gout, T *__restrict__ gy, int C, int H,
-                                                        int W, int al) {
+// NW = 4 normally; NW = 8 when the grid is small (at most two workgroups per CU),
+// which doubles the waves each SIMD has to hide latency with.
+template <typename T, int K, int MB, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void bwd_dy_kernel(const T *__restrict__ x,
+                                                                         const T *__restrict__ wg,
+                                                                         const T *__restrict__ gout,
+                                                                         T *__restrict__ gy, int C, int H, int W,
+                                                                         int al) {
     constexpr int r = (K - 1) / 2;
     constexpr int KK = K * K;
     constexpr bool BF = Elem<T>::is_bf16;
     constexpr int CK = BF ? 32 : 4;  // generator channels per k-step
-    __shared__ f32x4 red[3][4][64];  // one 16-channel block of the cross-wave sum at a time
+    __shared__ f32x4 red[NW - 1][4][64];  // one 16-channel block of the cross-wave sum at a time
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -70,8 +75,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
     const bool full = (C % CK == 0) && (cm0 + 16 * MB <= C) && (w0 + kCols <= W);
     const int ncq = (C + CK - 1) / CK;
     const int nitems = ncq * 3 * KK;  // (cq, b, t), t fastest
-    const int i0 = (int)((int64_t)nitems * wave / 4);
-    const int i1 = (int)((int64_t)nitems * (wave + 1) / 4);
+    const int i0 = (int)((int64_t)nitems * wave / NW);
+    const int i1 = (int)((int64_t)nitems * (wave + 1) / NW);
 
     if constexpr (!BF) {
         // Operands of one item, fetched one item ahead of its MFMAs.
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
         }
     }
 
-    // Fixed-order sum of the four waves' partial products, ((w0 + w1) + w2) + w3, one
+    // Fixed-order sum of the waves' partial products, ((w0 + w1) + w2) + ..., one
     // 16-channel block at a time through LDS.
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_kernel(const T *__restrict__ x,
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int k = 0; k < 3; ++k)
+            for (int k = 0; k < NW - 1; ++k)
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) acc[m][pb] += red[k][pb][lane];
         }
@@ -583,13 +588,21 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     if (gy != nullptr) {
         const dim3 grid((unsigned)nblk_dy);
         const int mb = (C >= 64) ? 4 : (C + 15) / 16;
-        auto args = [&](auto kern) {
-            hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const T *)x, (const T *)wg, (const T *)gout,
+        // eight waves per workgroup when the grid gives at most two workgroups per CU
+        const bool wide = nblk_dy <= 2 * kCUs;
+        auto args = [&](auto kern, int nw) {
+            hipLaunchKernelGGL(kern, grid, dim3(64 * nw), 0, stream, (const T *)x, (const T *)wg, (const T *)gout,
                                (T *)gy, C, H, W, iA);
         };
-        if (mb == 1) args(bwd_dy_kernel<T, K, 1>);
-        else if (mb == 2) args(bwd_dy_kernel<T, K, 2>);
-        else args(bwd_dy_kernel<T, K, 4>);
+        if (wide) {
+            if (mb == 1) args(bwd_dy_kernel<T, K, 1, 8>, 8);
+            else if (mb == 2) args(bwd_dy_kernel<T, K, 2, 8>, 8);
+            else args(bwd_dy_kernel<T, K, 4, 8>, 8);
+        } else {
+            if (mb == 1) args(bwd_dy_kernel<T, K, 1, 4>, 4);
+            else if (mb == 2) args(bwd_dy_kernel<T, K, 2, 4>, 4);
+            else args(bwd_dy_kernel<T, K, 4, 4>, 4);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
