@@ -32,6 +32,7 @@ namespace {
 constexpr int kSeg = 64;    // pixels per row segment (16 lanes x 4)
 constexpr int kChunk = 64;  // input channels per stage
 constexpr int kOutCh = 64;  // output channels per workgroup (16 per wave)
+constexpr int kCUs = 256;   // compute units of the chip (MI355X)
 
 template <typename T> struct DxStage;
 
@@ -41,13 +42,13 @@ template <> struct DxStage<float> {
     static constexpr int SUB = 4;             // 16-channel MFMA chunks per stage
     struct Regs { f32x4 v[4]; };
 
-    // Thread tid stages channel tid/4 of the chunk, pixels 16*(tid%4) .. +15 of the
-    // shifted segment starting at column ws0.
-    __device__ __forceinline__ static void load(Regs &R, const float *__restrict__ yn, int c_first, int C,
+    // Thread tid (0..255 within its wave group) stages channel tid/4 of the chunk,
+    // pixels 16*(tid%4) .. +15 of the shifted segment starting at column ws0.
+    __device__ __forceinline__ static void load(Regs &R, int tid, const float *__restrict__ yn, int c_first, int C,
                                                 int64_t HW, int64_t rowoff, int ws0, int W, bool row_ok,
                                                 bool fast, bool al) {
-        const int c = c_first + (threadIdx.x >> 2);
-        const int px = ws0 + 16 * (threadIdx.x & 3);
+        const int c = c_first + (tid >> 2);
+        const int px = ws0 + 16 * (tid & 3);
         const float *row = yn + (int64_t)(c < C ? c : 0) * HW + rowoff;
         const bool al4 = al && ((px & 3) == 0);  // 16-byte aligned runs (rows are, when al)
         if (fast) {
@@ -58,8 +59,8 @@ template <> struct DxStage<float> {
             for (int i = 0; i < 4; ++i) R.v[i] = load4_row(row, px + 4 * i, W, row_ok && c < C, al4);
         }
     }
-    __device__ __forceinline__ static void store(float *__restrict__ buf, const Regs &R) {
-        float *p = buf + (threadIdx.x >> 2) * ROW + 16 * (threadIdx.x & 3);
+    __device__ __forceinline__ static void store(float *__restrict__ buf, int tid, const Regs &R) {
+        float *p = buf + (tid >> 2) * ROW + 16 * (tid & 3);
 #pragma unroll
         for (int i = 0; i < 4; ++i) *(f32x4 *)(p + 4 * i) = R.v[i];
     }
@@ -105,24 +106,25 @@ template <> struct DxStage<bf16_t> {
         return u;
     }
 
-    // Thread tid stages channels 4*(tid/16) .. +3 of the chunk, pixels 4*(tid%16) .. +3.
-    __device__ __forceinline__ static void load(Regs &R, const bf16_t *__restrict__ yn, int c_first, int C,
+    // Thread tid (0..255 within its wave group) stages channels 4*(tid/16) .. +3 of
+    // the chunk, pixels 4*(tid%16) .. +3.
+    __device__ __forceinline__ static void load(Regs &R, int tid, const bf16_t *__restrict__ yn, int c_first, int C,
                                                 int64_t HW, int64_t rowoff, int ws0, int W, bool row_ok,
                                                 bool fast, bool al) {
-        const int px = ws0 + 4 * (threadIdx.x & 15);
+        const int px = ws0 + 4 * (tid & 15);
         const bool odd = (ws0 & 1) != 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = c_first + 4 * (threadIdx.x >> 4) + i;
+            const int c = c_first + 4 * (tid >> 4) + i;
             const bf16_t *row = yn + (int64_t)(c < C ? c : 0) * HW + rowoff;
             R.v[i] = run4(row, px, W, row_ok && c < C, fast, al && ((px & 3) == 0), al, odd);
         }
     }
-    __device__ __forceinline__ static void store(bf16_t *__restrict__ buf, const Regs &R) {
-        const int c4 = 4 * (threadIdx.x >> 4);
+    __device__ __forceinline__ static void store(bf16_t *__restrict__ buf, int tid, const Regs &R) {
+        const int c4 = 4 * (tid >> 4);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int P = 4 * (threadIdx.x & 15) + p;
+            const int P = 4 * (tid & 15) + p;
             u16x4 u;
             u[0] = R.v[0][p]; u[1] = R.v[1][p]; u[2] = R.v[2][p]; u[3] = R.v[3][p];
             *(u16x4 *)(buf + slot(P, c4 >> 3) + (c4 & 4)) = u;
@@ -139,16 +141,27 @@ template <> struct DxStage<bf16_t> {
     }
 };
 
-template <typename T, int K>
-__global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y, const T *__restrict__ wg,
-                                                        const T *__restrict__ bg, const T *__restrict__ gout,
-                                                        T *__restrict__ gx, int C, int H, int W, int al) {
+// NG = 1: four waves, one per 16-channel block, run every stage.  NG = 2 (small
+// grids, at most two workgroups per CU): two groups of four waves, each with its own
+// staging buffers, take the first and the second half of the stages in lockstep
+// (the shared barriers), and the second group's sums are added to the first's in a
+// fixed order at the end -- twice the waves per SIMD for the same tile.
+template <typename T, int K, int NG>
+__global__ __launch_bounds__(256 * NG, NG == 1 ? 2 : 1) void bwd_dx_kernel(const T *__restrict__ y,
+                                                                          const T *__restrict__ wg,
+                                                                          const T *__restrict__ bg,
+                                                                          const T *__restrict__ gout,
+                                                                          T *__restrict__ gx, int C, int H, int W,
+                                                                          int al) {
     using G = Gen<T>;
     using S = DxStage<T>;
     constexpr int r = (K - 1) / 2;
     constexpr int KK = K * K;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int grp = NG == 1 ? 0 : wave_all >> 2;                      // wave group
+    const int wave = NG == 1 ? wave_all : wave_all & 3;                // 16-channel block within it
+    const int tid = NG == 1 ? (int)threadIdx.x : (int)threadIdx.x & 255;  // thread within the group
     const int g = lane >> 4;
     const int j = lane & 15;
     // logical tile order: channel group fastest, then column segment, row, image
@@ -176,13 +189,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     const T *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
     const int nqq = (C + kChunk - 1) / kChunk;
     const int nstage = 3 * KK * nqq;
+    // this group's stages [sb, se), whole taps (all nqq chunks of a tap stay in one
+    // group); every group runs `nit` lockstep iterations
+    const int cpg = (3 * KK + NG - 1) / NG;  // taps per group
+    const int nit = cpg * nqq;
+    const int sb = grp * nit;
+    const int se = min(nstage, sb + nit);
 
     // float32 keeps few registers live (weight fragments one MFMA chunk ahead, G_b
     // loaded at the start of the stage that uses it: a stage holds 2048 MFMA cycles),
     // so four workgroups fit a CU; bfloat16 stages are short, so everything a stage
     // needs is fetched one whole stage ahead.
     constexpr bool AHEAD = Elem<T>::is_bf16;
-    __shared__ __align__(16) T stage[2][S::ELEMS];
+    __shared__ __align__(16) T stage[NG][2][S::ELEMS];
     // bfloat16: the biases of this workgroup's channels for every tap, staged once
     // (bl[(b*KK + t)*64 + ch]); float32 loads a tap's biases with its G_b.
     __shared__ float bl[AHEAD ? 3 * KK * kOutCh : 1];
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
         const int ws0 = w0 - sh.dc;
         const int64_t rowoff = (int64_t)(sh.row_ok ? sh.hs : 0) * W;
         const bool fast = (kChunk * qq + kChunk <= C) && sh.row_ok && ws0 - (ws0 & 1) >= 0 && ws0 + kSeg <= W;
-        S::load(R, yn, kChunk * qq, C, HW, rowoff, ws0, W, sh.row_ok, fast, aligned4);
+        S::load(R, tid, yn, kChunk * qq, C, HW, rowoff, ws0, W, sh.row_ok, fast, aligned4);
     };
     // weight fragment of MFMA chunk u of stage (combo, qq) for this wave's 16 generator rows
     auto load_A1 = [&](int combo, int qq, int u, typename G::AFrag &a) {
@@ -281,17 +300,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
         }
     };
 
+    const bool grp_on = NG == 1 || sb < se;  // wave-uniform: the group has stages
+    int combo = sb / nqq, qq = sb - (sb / nqq) * nqq;  // current stage
     typename S::Regs R;
-    load_stage(0, 0, R);
-    S::store(stage[0], R);
+    if (grp_on) {
+        load_stage(combo, qq, R);
+        S::store(stage[grp][0], tid, R);
+    }
     typename G::AFrag acur[AHEAD ? S::SUB : 1];
     f32x4 gcur[4], gnext[4], bcur = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wave_on) {
+    if (wave_on && grp_on) {
         if constexpr (AHEAD) {
-            load_A(0, 0, acur);
-            load_G(0, gcur);
+            load_A(combo, qq, acur);
+            load_G(combo, gcur);
         } else {
-            load_A1(0, 0, 0, acur[0]);
+            load_A1(combo, qq, 0, acur[0]);
         }
     }
     float dacc[4][4];
@@ -302,10 +325,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
     f32x4 acc[4];
     __syncthreads();
 
-    int combo = 0, qq = 0;  // current stage
 #pragma unroll 1
-    for (int s = 0; s < nstage; ++s) {
-        const bool more = s + 1 < nstage;
+    for (int it = 0; it < nit; ++it) {
+        const int s = sb + it;
+        const bool act = NG == 1 || s < se;  // wave-uniform: this group has a stage this round
+        const bool more = s + 1 < se;
         const int qn = qq + 1 == nqq ? 0 : qq + 1;  // next stage
         const int cn = qn == 0 ? combo + 1 : combo;
         typename G::AFrag anext[S::SUB];  // bfloat16: the next stage's fragments
@@ -318,9 +342,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
                 }
             }
         }
-        if (wave_on) {
+        if (wave_on && act) {
             const bool last = qq == nqq - 1;  // the tap's last chunk: its G_b term follows
-            const T *buf = stage[s & 1];
+            const T *buf = stage[grp][it & 1];
             const int left = C - kChunk * qq;
             const int nsub = left >= kChunk ? S::SUB : (left + G::CH - 1) / G::CH;
             if (qq == 0) {
@@ -370,12 +394,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_kernel(const T *__restrict__ y,
                 }
             }
         }
-        if (more) S::store(stage[(s + 1) & 1], R);
+        if (more) S::store(stage[grp][(it + 1) & 1], tid, R);
         __syncthreads();
         combo = cn;
         qq = qn;
     }
 
+    if constexpr (NG == 2) {
+        // the second group's sums, through its (now idle) staging buffers, added to
+        // the first group's: dX = G_x + (first half of the taps + second half)
+        float *xfer = reinterpret_cast<float *>(&stage[1][0][0]);
+        if (grp == 1 && wave_on) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                *(f32x4 *)(xfer + ((wave * 64 + lane) * 4 + v) * 4) =
+                    f32x4{dacc[v][0], dacc[v][1], dacc[v][2], dacc[v][3]};
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        if (wave_on) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const f32x4 o = *(const f32x4 *)(xfer + ((wave * 64 + lane) * 4 + v) * 4);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += o[pb];
+            }
+        }
+    }
     if (!wave_on) return;
     const int64_t rowoff = (int64_t)h * W;
 #pragma unroll
@@ -395,8 +440,13 @@ hipError_t launch_dx_t(const void *y, const void *wg, const void *bg, const void
                        int W, bool al, hipStream_t stream) {
     const int64_t nblk = bwd_dx_blocks(N, C, H, W);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dx_kernel<T, K>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T *)y,
-                       (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
+    // two wave groups per workgroup when the grid gives at most two workgroups per CU
+    if (nblk <= 2 * kCUs)
+        hipLaunchKernelGGL((bwd_dx_kernel<T, K, 2>), dim3((unsigned)nblk), dim3(512), 0, stream, (const T *)y,
+                           (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
+    else
+        hipLaunchKernelGGL((bwd_dx_kernel<T, K, 1>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T *)y,
+                           (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
     return hipGetLastError();
 }
 
