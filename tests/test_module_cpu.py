@@ -14,6 +14,8 @@ def test_thresholds_table():
                 assert (mode, dt, K) in AUTO_MIN_TOKENS
     assert auto_min_tokens(True, F32, 1) == auto_min_tokens(True, F32, 3)
     assert auto_min_tokens(True, BF16, 5) == 65536  # measured: fused faster only from 256^2
+    assert auto_min_tokens(True, F32, 5) == 16384   # measured: fused faster from 128^2
+    assert auto_min_tokens(True, F32, 3) == 1       # measured: fused faster at every size
 
 
 def test_inference_path():
@@ -31,9 +33,10 @@ def test_inference_path():
 def test_training_path():
     big = 1 << 20
     assert choose_path(True, big, 3, F32, F32, F32, False) == "fused"
-    assert choose_path(True, 100, 3, F32, F32, F32, False) == "materialised"
-    assert choose_path(True, 100, 3, BF16, BF16, BF16, False) == "materialised"
-    assert choose_path(True, 2048, 3, BF16, BF16, BF16, False) == "fused"
+    assert choose_path(True, 100, 3, F32, F32, F32, False) == "fused"
+    assert choose_path(True, 100, 5, F32, F32, F32, False) == "materialised"
+    assert choose_path(True, 16384, 5, F32, F32, F32, False) == "fused"
+    assert choose_path(True, 100, 3, BF16, BF16, BF16, False) == "fused"
     assert choose_path(True, 36864, 5, BF16, BF16, BF16, False) == "materialised"
     assert choose_path(True, big, 5, BF16, BF16, BF16, False) == "fused"
     assert choose_path(True, big, 3, F32, F32, F32, True) == "materialised"           # autocast
