@@ -52,6 +52,9 @@ BWD_CASES = [
     ("c70_streamed", (S_(1, 70, 12, 20, 3), 210)), ("c2_k5_tall", (S_(2, 2, 37, 6, 5), 212)),
     ("c48_ragged", (S_(1, 48, 12, 70, 3), 213)), ("c64_w200_k5", (S_(1, 64, 9, 200, 5), 214)),
     ("batch4_c64_64", (S_(4, 64, 64, 64, 3), 215)),
+    # grids of more than two workgroups per CU (four-wave dY, one wave group in dX)
+    # at K = 5 and with a partial channel block count (C = 24, ragged rows)
+    ("k5_large_grid", (S_(1, 64, 160, 256, 5), 216)), ("c24_large_grid", (S_(1, 24, 150, 300, 3), 217)),
 ]
 
 
