@@ -218,6 +218,33 @@ def test_partial_counts_agree(S, shape, dt):
     assert_close(f64(gw), ref, 1e-6 if dt == "f32" else 4e-3, "reduce of partials")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_partials_follow_documented_ranges(dt):
+    """Each partial holds the sum over the token range the header documents: range s
+    starts at floor(T*s/S) rounded down to 64 (float32) / 128 (bfloat16) tokens and
+    the last ends at T.  The expected partial s is the oracle's gradient with
+    grad_out zeroed outside range s (a token's dK, hence its contribution, is
+    proportional to grad_out at that token)."""
+    dtype = DT[dt]
+    shape, S = S_(1, 8, 37, 45, 3), 5
+    K, T = shape.K, shape.N * shape.H * shape.W
+    h = inputs(shape, 303, dtype, grad=True)
+    a = {k: f64(v) for k, v in h.items()}
+    announce("partial ranges", S, shape, dt)
+    _, _, _, _, pw, pb = gpu_bwd(dev(h), K, S=S)
+    step = 64 if dt == "f32" else 128
+    starts = [T * s // S // step * step for s in range(S)] + [T]
+    assert len(set(starts)) == S + 1  # the case has no empty range
+    tol = TOL[dtype]["grad"]
+    for s in range(S):
+        mask = np.zeros(T)
+        mask[starts[s]:starts[s + 1]] = 1.0
+        g = a["grad_out"] * mask.reshape(shape.N, 1, shape.H, shape.W)
+        _, _, dW, db = orc().fused_bwd(a["x"], a["y"], a["weight"], a["bias"], g, K)
+        assert_close(f64(pw[s]), dW, tol, f"dweight partial {s} [{starts[s]}, {starts[s + 1]})")
+        assert_close(f64(pb[s]), db, tol, f"dbias partial {s} [{starts[s]}, {starts[s + 1]})")
+
+
 @pytest.mark.parametrize("name", ["nonaligned", "fused_training_128_k5"])
 def test_bitwise_deterministic(name):
     shape, block = synth.WORKLOADS[name]
