@@ -402,7 +402,9 @@ __global__ __launch_bounds__(256 * NG, NG == 1 ? 2 : 1) void bwd_dx_kernel(const
 
     if constexpr (NG == 2) {
         // the second group's sums, through its (now idle) staging buffers, added to
-        // the first group's: dX = G_x + (first half of the taps + second half)
+        // the first group's: dX = G_x + (first half of the taps + second half).  The
+        // buffers are reused as float storage (16 KB, within both dtypes' 2 * ELEMS);
+        // the barriers before the stores and before the loads order every access.
         float *xfer = reinterpret_cast<float *>(&stage[1][0][0]);
         if (grp == 1 && wave_on) {
 #pragma unroll
