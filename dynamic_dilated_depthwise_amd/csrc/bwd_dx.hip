@@ -141,13 +141,13 @@ template <> struct DxStage<bf16_t> {
     }
 };
 
-// NG = 1: four waves, one per 16-channel block, run every stage.  NG = 2 (small
-// grids, at most two workgroups per CU): two groups of four waves, each with its own
-// staging buffers, take the first and the second half of the stages in lockstep
-// (the shared barriers), and the second group's sums are added to the first's in a
-// fixed order at the end -- twice the waves per SIMD for the same tile.
+// NG = 1: four waves, one per 16-channel block, run every stage.  NG = 2 or 4 (small
+// grids): NG groups of four waves, each with its own staging buffers, take
+// consecutive whole-tap shares of the stages in lockstep (the shared barriers), and
+// the other groups' sums are added to the first's in group order at the end -- NG
+// times the waves per SIMD for the same tile.
 template <typename T, int K, int NG>
-__global__ __launch_bounds__(256 * NG, NG == 1 ? 2 : 1) void bwd_dx_kernel(const T *__restrict__ y,
+__global__ __launch_bounds__(256 * NG, NG == 4 ? 4 : (NG == 1 ? 2 : 1)) void bwd_dx_kernel(const T *__restrict__ y,
                                                                           const T *__restrict__ wg,
                                                                           const T *__restrict__ bg,
                                                                           const T *__restrict__ gout,
@@ -400,26 +400,31 @@ __global__ __launch_bounds__(256 * NG, NG == 1 ? 2 : 1) void bwd_dx_kernel(const
         qq = qn;
     }
 
-    if constexpr (NG == 2) {
-        // the second group's sums, through its (now idle) staging buffers, added to
-        // the first group's: dX = G_x + (first half of the taps + second half).  The
-        // buffers are reused as float storage (16 KB, within both dtypes' 2 * ELEMS);
-        // the barriers before the stores and before the loads order every access.
-        float *xfer = reinterpret_cast<float *>(&stage[1][0][0]);
-        if (grp == 1 && wave_on) {
+    if constexpr (NG > 1) {
+        // the other groups' sums, each through its own (now idle) staging buffers,
+        // added to the first group's in group order: dX = G_x + ((taps of group 0 +
+        // taps of group 1) + ...).  The buffers are reused as float storage (16 KB,
+        // within both dtypes' 2 * ELEMS); the barriers before the stores and before
+        // the loads order every access.
+        if (grp > 0 && wave_on) {
+            float *xfer = reinterpret_cast<float *>(&stage[grp][0][0]);
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 *(f32x4 *)(xfer + ((wave * 64 + lane) * 4 + v) * 4) =
                     f32x4{dacc[v][0], dacc[v][1], dacc[v][2], dacc[v][3]};
         }
         __syncthreads();
-        if (grp == 1) return;
+        if (grp > 0) return;
         if (wave_on) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const f32x4 o = *(const f32x4 *)(xfer + ((wave * 64 + lane) * 4 + v) * 4);
+            for (int k = 1; k < NG; ++k) {
+                const float *xfer = reinterpret_cast<const float *>(&stage[k][0][0]);
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += o[pb];
+                for (int v = 0; v < 4; ++v) {
+                    const f32x4 o = *(const f32x4 *)(xfer + ((wave * 64 + lane) * 4 + v) * 4);
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) dacc[v][pb] += o[pb];
+                }
             }
         }
     }
@@ -442,8 +447,12 @@ hipError_t launch_dx_t(const void *y, const void *wg, const void *bg, const void
                        int W, bool al, hipStream_t stream) {
     const int64_t nblk = bwd_dx_blocks(N, C, H, W);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // two wave groups per workgroup when the grid gives at most two workgroups per CU
-    if (nblk <= 2 * kCUs)
+    // more wave groups per workgroup on small grids: four when the grid gives at most
+    // one workgroup per CU, two when at most two
+    if (nblk <= kCUs)
+        hipLaunchKernelGGL((bwd_dx_kernel<T, K, 4>), dim3((unsigned)nblk), dim3(1024), 0, stream, (const T *)y,
+                           (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
+    else if (nblk <= 2 * kCUs)
         hipLaunchKernelGGL((bwd_dx_kernel<T, K, 2>), dim3((unsigned)nblk), dim3(512), 0, stream, (const T *)y,
                            (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
     else
