@@ -24,9 +24,8 @@ materialised path, ``None`` (the default) picks the fused path when it is eligib
 and the token count N*H*W reaches the threshold for (mode, dtype, K) in
 ``AUTO_MIN_TOKENS``.  The page's thresholds were tuned on its own GPU; these come
 from timing both paths on MI355X (``bench_module.py``, B=1, C=64, 16^2 .. 256^2):
-training with K = 3 is fused at every size (fp32 and bf16), fp32 training with
-K = 5 from 128^2 = 16384 tokens, bf16 training with K = 5 from 256^2 = 65536 tokens,
-and inference is fused at every size.  The fused path also needs about a tenth of the
+training is fused at every size except fp32 with K = 5, which is fused from
+96^2 = 9216 tokens, and inference is fused at every size.  The fused path also needs about a tenth of the
 temporary memory (the tap tensor and its gradient are never stored).  There is no
 CPU path: CPU tensors raise.
 """
@@ -43,8 +42,8 @@ __all__ = ["DDPMFused", "DDPMFilter", "ddpm_fused", "ddpm_filter", "choose_path"
 # None: never (MI355X timings of bench_module.py; K = 1 follows K = 3).
 _F32, _BF16 = torch.float32, torch.bfloat16
 AUTO_MIN_TOKENS = {
-    ("train", _F32, 3): 1, ("train", _F32, 5): 16384,
-    ("train", _BF16, 3): 1, ("train", _BF16, 5): 65536,
+    ("train", _F32, 3): 1, ("train", _F32, 5): 9216,
+    ("train", _BF16, 3): 1, ("train", _BF16, 5): 1,
     ("infer", _F32, 3): 1, ("infer", _F32, 5): 1,
     ("infer", _BF16, 3): 1, ("infer", _BF16, 5): 1,
 }

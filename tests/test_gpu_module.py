@@ -91,7 +91,7 @@ def test_training(name, shape, seed, dt, path):
 
 def test_auto_and_mismatch_paths():
     """Automatic mode follows the measured thresholds (K=3 trains fused at every
-    size, fp32 K=5 below 128^2 materialised); a dtype mismatch takes the
+    size, fp32 K=5 below 96^2 materialised); a dtype mismatch takes the
     materialised path and computes in the generator's dtype."""
     shape, seed = S_(1, 16, 10, 12, 5), 405
     sb = S_(1, 16, 32, 40, 3)  # 1280 tokens
