@@ -34,7 +34,7 @@ constexpr int kCols = 64;  // 16 lanes x 4 pixels
 // NW = 4 normally; NW = 8 when the grid is small (at most two workgroups per CU),
 // which doubles the waves each SIMD has to hide latency with.
 template <typename T, int K, int MB, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void bwd_dy_kernel(const T *__restrict__ x,
+__global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : (NW == 4 ? 2 : 1)) void bwd_dy_kernel(const T *__restrict__ x,
                                                                          const T *__restrict__ wg,
                                                                          const T *__restrict__ gout,
                                                                          T *__restrict__ gy, int C, int H, int W,
@@ -588,13 +588,21 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
     if (gy != nullptr) {
         const dim3 grid((unsigned)nblk_dy);
         const int mb = (C >= 64) ? 4 : (C + 15) / 16;
-        // eight waves per workgroup when the grid gives at most two workgroups per CU
+        // eight waves per workgroup when the grid gives at most two workgroups per CU;
+        // sixteen (float32) when at most one
         const bool wide = nblk_dy <= 2 * kCUs;
+        const bool wider = !Elem<T>::is_bf16 && nblk_dy <= kCUs;
         auto args = [&](auto kern, int nw) {
             hipLaunchKernelGGL(kern, grid, dim3(64 * nw), 0, stream, (const T *)x, (const T *)wg, (const T *)gout,
                                (T *)gy, C, H, W, iA);
         };
-        if (wide) {
+        if (wider) {
+            if constexpr (!Elem<T>::is_bf16) {  // (bfloat16 would spill at 128 registers)
+                if (mb == 1) args(bwd_dy_kernel<T, K, 1, 16>, 16);
+                else if (mb == 2) args(bwd_dy_kernel<T, K, 2, 16>, 16);
+                else args(bwd_dy_kernel<T, K, 4, 16>, 16);
+            }
+        } else if (wide) {
             if (mb == 1) args(bwd_dy_kernel<T, K, 1, 8>, 8);
             else if (mb == 2) args(bwd_dy_kernel<T, K, 2, 8>, 8);
             else args(bwd_dy_kernel<T, K, 4, 8>, 8);
