@@ -12,6 +12,8 @@
 //   (see gen_mma.hpp), adds the bias, rounds the taps to the dtype, and
 //   multiplies them with x at the dilated offset, read from an LDS copy of the
 //   x tile with its 5*(K-1)/2 halo.  The three branch sums stay in registers.
+// bfloat16 grids with one workgroup per CU instead run workgroups of three such
+// four-wave groups, one per dilation branch, sharing the staged x tile.
 // y is read once per wave into registers (the MFMA B operand is the same for
 // all 3*K*K generator blocks) when C <= 64; larger C streams it per block.
 #include <algorithm>
@@ -135,8 +137,8 @@ __device__ __forceinline__ void store4_bits(T *__restrict__ row, int w, int W, f
     }
 }
 
-template <typename T, int K, int KQ, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__ x, const T *__restrict__ y,
+template <typename T, int K, int KQ, bool SPLIT, bool GRP3>
+__global__ __launch_bounds__(GRP3 ? 768 : 256, GRP3 ? 3 : 2) void fused_fwd_kernel(const T *__restrict__ x, const T *__restrict__ y,
                                                            const T *__restrict__ wg, const T *__restrict__ bg,
                                                            T *__restrict__ out, int C, int H, int W, int al) {
     using G = Gen<T>;
@@ -146,7 +148,8 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     extern __shared__ float xs[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int wave = GRP3 ? (wave_all & 3) : wave_all;  // the tile row this wave computes
     const int g = lane >> 4;
     const int j = lane & 15;
     const int nCB = (C + 15) >> 4;
@@ -156,7 +159,8 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const int ncolt = (W + kTileCols - 1) / kTileCols;
     const int nbands = (H + kTileRows - 1) / kTileRows;
     int L = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int bsel = SPLIT ? L % 3 : -1;  // the branch this workgroup computes, -1: all
+    // the branch this workgroup (SPLIT) or wave group (GRP3) computes, -1: all
+    const int bsel = SPLIT ? L % 3 : (GRP3 ? (wave_all >> 2) : -1);
     if (SPLIT) L /= 3;
     const int c0 = (L % nCB) * 16;
     L /= nCB;
@@ -170,18 +174,20 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
 
     const T *__restrict__ xn = x + (int64_t)n * C * HW;
     const T *__restrict__ yn = y + (int64_t)n * C * HW;
-    stage_x_tile<T, K>(xs, xn, c0, C, H, W, HW, h0, w0, aligned4);
     // bias slice: bl[(b*KK + t)*16 + ch] = bias[(b*C + c0 + ch)*KK + t]
     float *bl = xs + 16 * X::PLANE;
+    if (!GRP3 || wave_all < 4) {  // the first 256 threads stage the shared tile
+        stage_x_tile<T, K>(xs, xn, c0, C, H, W, HW, h0, w0, aligned4);
 #pragma unroll
-    for (int k = 0; k < (X::BIAS + 255) / 256; ++k) {
-        const int i = k * 256 + (int)threadIdx.x;
-        if (i >= X::BIAS) break;
-        const int combo = i >> 4;
-        const int c = c0 + (i & 15);
-        const int b = combo / KK;
-        const int t = combo - b * KK;
-        bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+        for (int k = 0; k < (X::BIAS + 255) / 256; ++k) {
+            const int i = k * 256 + (int)threadIdx.x;
+            if (i >= X::BIAS) break;
+            const int combo = i >> 4;
+            const int c = c0 + (i & 15);
+            const int b = combo / KK;
+            const int t = combo - b * KK;
+            bl[i] = c < C ? Elem<T>::to_f32(bg[(int64_t)(b * C + c) * KK + t]) : 0.f;
+        }
     }
 
     const int h = h0 + wave;
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
                            f32x4{ob[v][0], ob[v][1], ob[v][2], ob[v][3]}, aligned4);
         }
     };
-    if (row_ok && (!SPLIT || bsel == 0)) {
+    if (row_ok && (!(SPLIT || GRP3) || bsel == 0)) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int c = c0 + 4 * g + v;
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
     const int aoff = cA * KK * C + 4 * (Elem<T>::is_bf16 ? 2 : 1) * g;  // lane's offset inside a (b, t) slice
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
-        if (SPLIT && b != bsel) continue;  // wave-uniform
+        if ((SPLIT || GRP3) && b != bsel) continue;  // wave-uniform
         const int D = dilation(b);
         // Generator-row operand of tap t of this branch.
         auto fetch = [&](int t, typename G::AFrag (&af)[KQ > 0 ? KQ : 1]) {
@@ -289,13 +295,18 @@ __global__ __launch_bounds__(256, 2) void fused_fwd_kernel(const T *__restrict__
 template <typename T, int K, int KQ>
 static hipError_t launch_fused_t(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
                                  int C, int H, int W, bool al, hipStream_t stream) {
-    auto kern = fused_fwd_kernel<T, K, KQ, false>;
-    auto kern_split = fused_fwd_kernel<T, K, KQ, true>;
+    auto kern = fused_fwd_kernel<T, K, KQ, false, false>;
+    auto kern_split = fused_fwd_kernel<T, K, KQ, true, false>;
+    // bfloat16 only: a workgroup of three four-wave groups, one per branch (float32's
+    // longer MFMAs keep the pipe busy with fewer waves; measured no gain there)
+    auto kern_grp3 = fused_fwd_kernel<T, K, KQ, false, Elem<T>::is_bf16>;
     const size_t lds = XTile<K>::bytes;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e == hipSuccess)
             e = hipFuncSetAttribute((const void *)kern_split, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess && Elem<T>::is_bf16)
+            e = hipFuncSetAttribute((const void *)kern_grp3, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int64_t nblk = (int64_t)((W + kTileCols - 1) / kTileCols) * ((H + kTileRows - 1) / kTileRows) * N *
@@ -307,6 +318,11 @@ static hipError_t launch_fused_t(const void *x, const void *y, const void *wg, c
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, (int64_t)(160 * 1024) / (int64_t)lds));
     if (nblk * 3 <= kCUs * per_cu)
         hipLaunchKernelGGL(kern_split, dim3((unsigned)(nblk * 3)), dim3(256), lds, stream, (const T *)x, (const T *)y,
+                           (const T *)wg, (const T *)bg, (T *)out, C, H, W, al ? 1 : 0);
+    // bfloat16 with one workgroup per CU (the K = 5 tile's LDS, or a grid of at most one
+    // per CU): three branch groups share the workgroup's x tile, tripling the waves
+    else if (Elem<T>::is_bf16 && (per_cu == 1 || nblk <= kCUs))
+        hipLaunchKernelGGL(kern_grp3, dim3((unsigned)nblk), dim3(768), lds, stream, (const T *)x, (const T *)y,
                            (const T *)wg, (const T *)bg, (T *)out, C, H, W, al ? 1 : 0);
     else
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), lds, stream, (const T *)x, (const T *)y,
