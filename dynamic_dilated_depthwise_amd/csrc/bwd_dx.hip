@@ -146,7 +146,7 @@ template <> struct DxStage<bf16_t> {
 // consecutive whole-tap shares of the stages in lockstep (the shared barriers), and
 // the other groups' sums are added to the first's in group order at the end -- NG
 // times the waves per SIMD for the same tile.
-template <typename T, int K, int NG>
+template <typename T, int K, int NG, bool FULLW>
 __global__ __launch_bounds__(256 * NG, NG == 4 ? 4 : (NG == 1 ? 2 : 1)) void bwd_dx_kernel(const T *__restrict__ y,
                                                                           const T *__restrict__ wg,
                                                                           const T *__restrict__ bg,
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256 * NG, NG == 4 ? 4 : (NG == 1 ? 2 : 1)) void bwd
         const int b = combo / KK;
         const int t = combo - b * KK;
         const int q = S::SUB * qq + u;  // MFMA chunk of G::CH input channels
-        if (full && kChunk * qq + kChunk <= C) {
+        if (FULLW || (full && kChunk * qq + kChunk <= C)) {
             a = G::load_A_off(wg + ((int64_t)b * C * KK + t) * C, cA * KK * C + G::CH * q + (G::CH / 4) * g);
         } else {
             const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
@@ -369,7 +369,18 @@ __global__ __launch_bounds__(256 * NG, NG == 4 ? 4 : (NG == 1 ? 2 : 1)) void bwd
                 }
 #pragma unroll
                 for (int u = 0; u < S::SUB; ++u) {
-                    if (u < nsub) {
+                    if (FULLW) {
+                        // Whole chunks, aligned weights: the next fragment (this one again
+                        // after the last) is one load on every path, so the wait before the
+                        // MFMAs can leave it in flight (with loads on some paths only, the
+                        // compiler has to wait for all of them there).
+                        typename G::AFrag an;
+                        const bool in_stage = u + 1 < S::SUB;
+                        load_A1(in_stage ? combo : (more ? cn : combo), in_stage ? qq : (more ? qn : qq),
+                                in_stage ? u + 1 : (more ? 0 : u), an);
+                        G::mma(acc, acur[0], S::frag(buf, u, g, j));
+                        acur[0] = an;
+                    } else if (u < nsub) {
                         typename G::AFrag an;
                         const bool in_stage = u + 1 < nsub;
                         if (in_stage) load_A1(combo, qq, u + 1, an);
@@ -449,15 +460,22 @@ hipError_t launch_dx_t(const void *y, const void *wg, const void *bg, const void
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     // more wave groups per workgroup on small grids: four when the grid gives at most
     // one workgroup per CU, two when at most two
-    if (nblk <= kCUs)
-        hipLaunchKernelGGL((bwd_dx_kernel<T, K, 4>), dim3((unsigned)nblk), dim3(1024), 0, stream, (const T *)y,
-                           (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
-    else if (nblk <= 2 * kCUs)
-        hipLaunchKernelGGL((bwd_dx_kernel<T, K, 2>), dim3((unsigned)nblk), dim3(512), 0, stream, (const T *)y,
-                           (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
-    else
-        hipLaunchKernelGGL((bwd_dx_kernel<T, K, 1>), dim3((unsigned)nblk), dim3(256), 0, stream, (const T *)y,
-                           (const T *)wg, (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
+    // float32 with whole 64-channel chunks and aligned rows: single-path weight prefetch
+    const bool fullw = !Elem<T>::is_bf16 && al && C % kChunk == 0 && (int64_t)H * W < (int64_t(1) << 26);
+    auto launch = [&](auto kern, int threads) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), 0, stream, (const T *)y, (const T *)wg,
+                           (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
+    };
+    if (nblk <= kCUs) {
+        if (fullw) launch(bwd_dx_kernel<T, K, 4, !Elem<T>::is_bf16>, 1024);
+        else launch(bwd_dx_kernel<T, K, 4, false>, 1024);
+    } else if (nblk <= 2 * kCUs) {
+        if (fullw) launch(bwd_dx_kernel<T, K, 2, !Elem<T>::is_bf16>, 512);
+        else launch(bwd_dx_kernel<T, K, 2, false>, 512);
+    } else {
+        if (fullw) launch(bwd_dx_kernel<T, K, 1, !Elem<T>::is_bf16>, 256);
+        else launch(bwd_dx_kernel<T, K, 1, false>, 256);
+    }
     return hipGetLastError();
 }
 
