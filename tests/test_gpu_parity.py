@@ -55,6 +55,9 @@ BWD_CASES = [
     # grids of more than two workgroups per CU (four-wave dY, one wave group in dX)
     # at K = 5 and with a partial channel block count (C = 24, ragged rows)
     ("k5_large_grid", (S_(1, 64, 160, 256, 5), 216)), ("c24_large_grid", (S_(1, 24, 150, 300, 3), 217)),
+    # two 64-channel blocks at K = 1, and a grid of two workgroups per CU (eight-wave
+    # dY, two wave groups in dX) on the workload's channel count
+    ("c128_k1_w64", (S_(1, 128, 12, 64, 1), 218)), ("c64_mid_grid", (S_(1, 64, 96, 192, 3), 219)),
 ]
 
 
