@@ -79,55 +79,52 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : (NW == 4 ? 2 : 1)) void bwd
     const int i1 = (int)((int64_t)nitems * (wave + 1) / NW);
 
     if constexpr (!BF) {
-        // Operands of one item, fetched one item ahead of its MFMAs.
-        struct Ops {
-            f32x4 gb, xs;
-            float a[MB];
-        };
-        auto fetch = [&](int i, Ops &o) {
-            const int t = i % KK;
-            const int pr = i / KK;
-            const int b = pr % 3;
-            const int c = CK * (pr / 3) + g;
-            const bool c_ok = c < C;
-            const int D = dilation(b);
-            const int ki = t / K;
-            const int kj = t - ki * K;
-            const int hh = h + (ki - r) * D;
-            const int dc = (kj - r) * D;
-            if (full && hh >= 0 && hh < H && w0 + dc - (dc & 1) >= 0 && w0 + kCols - 1 + dc < W) {  // wave-uniform
-                o.gb = load4_unchecked(gn + (int64_t)((1 + b) * C + c) * HW + rowoff, w, aligned4, true, false);
-                o.xs = load4_unchecked(xn + (int64_t)c * HW + (int64_t)hh * W, w + dc, aligned4 && ((dc & 3) == 0),
-                                       true, false);
-                const T *wrow = wg + ((int64_t)(b * C + c) * KK + t) * C + cm0 + j;
-#pragma unroll
-                for (int m = 0; m < MB; ++m) o.a[m] = wrow[16 * m];
-                return;
-            }
-            const bool rok = c_ok && hh >= 0 && hh < H;
-            o.gb = load4_row(gn + (int64_t)((1 + b) * C + (c_ok ? c : 0)) * HW + rowoff, w, W, c_ok, aligned4);
-            o.xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(rok ? hh : 0) * W, w + dc, W, rok,
-                             aligned4 && ((dc & 3) == 0));
-            const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                const int cp = cm0 + 16 * m + j;
-                o.a[m] = (c_ok && cp < C) ? wrow[cp] : 0.f;
-            }
-        };
-        // the next item's operands are in flight during this item's MFMAs (one item
-        // ahead keeps the kernel at four workgroups per CU)
-        Ops n1;
-        if (i0 < i1) fetch(i0, n1);
+        // The wave's items are walked by (channel chunk, branch) pair, then tap: G_b at
+        // the output row is loaded once per pair and the pair's indices and base
+        // pointers are formed once.  Items keep their order, so the sums do too.
+        const int p0 = i0 / KK;
+        const int p1 = (i1 + KK - 1) / KK;
 #pragma unroll 1
-        for (int i = i0; i < i1; ++i) {
-            const Ops cur = n1;
-            if (i + 1 < i1) fetch(i + 1, n1);
+        for (int p = p0; p < p1; ++p) {
+            const int b = p % 3;
+            const int c = CK * (p / 3) + g;
+            const bool c_ok = c < C;
+            const int cs = c_ok ? c : 0;
+            const int D = dilation(b);
+            const int tlo = i0 - p * KK;  // the pair's taps in [tlo, thi) belong to this wave
+            const int thi = i1 - p * KK;
+            const f32x4 gb = full ? load4_unchecked(gn + (int64_t)((1 + b) * C + c) * HW + rowoff, w, aligned4, true,
+                                                    false)
+                                  : load4_row(gn + (int64_t)((1 + b) * C + cs) * HW + rowoff, w, W, c_ok, aligned4);
+            const T *__restrict__ xc = xn + (int64_t)cs * HW;
+            const T *__restrict__ wb = wg + (int64_t)(b * C + cs) * KK * C;
+            const int ta = max(tlo, 0), tb = min(thi, KK);
+#pragma unroll 1
+            for (int t = ta; t < tb; ++t) {
+                const int ki = t / K;
+                const int kj = t - ki * K;
+                const int hh = h + (ki - r) * D;
+                const int dc = (kj - r) * D;
+                f32x4 xs;
+                float a[MB];
+                if (full && hh >= 0 && hh < H && w0 + dc - (dc & 1) >= 0 && w0 + kCols - 1 + dc < W) {  // wave-uniform
+                    xs = load4_unchecked(xc + (int64_t)hh * W, w + dc, aligned4 && ((dc & 3) == 0), true, false);
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
+                    for (int m = 0; m < MB; ++m) a[m] = wb[t * C + cm0 + j + 16 * m];
+                } else {
+                    const bool rok = c_ok && hh >= 0 && hh < H;
+                    xs = load4_row(xc + (int64_t)(rok ? hh : 0) * W, w + dc, W, rok, aligned4 && ((dc & 3) == 0));
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb)
-                    acc[m][pb] = mfma_16x16x4_f32(cur.a[m], cur.gb[pb] * cur.xs[pb], acc[m][pb]);
+                    for (int m = 0; m < MB; ++m) {
+                        const int cp = cm0 + 16 * m + j;
+                        a[m] = (c_ok && cp < C) ? wb[t * C + cp] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x4_f32(a[m], gb[pb] * xs[pb], acc[m][pb]);
+            }
         }
     } else {
         f32x4 gb[8];
