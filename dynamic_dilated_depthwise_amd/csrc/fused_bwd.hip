@@ -127,71 +127,72 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : (NW == 4 ? 2 : 1)) void bwd
             }
         }
     } else {
-        f32x4 gb[8];
-        int cur_pair = -1;
+        // as for float32: by (channel chunk, branch) pair, then tap
+        const int p0 = i0 / KK;
+        const int p1 = (i1 + KK - 1) / KK;
 #pragma unroll 1
-        for (int i = i0; i < i1; ++i) {
-            const int t = i % KK;
-            const int pr = i / KK;
-            const int b = pr % 3;
-            const int cq = pr / 3;
+        for (int p = p0; p < p1; ++p) {
+            const int b = p % 3;
+            const int cq = p / 3;
             const int D = dilation(b);
-            if (pr != cur_pair) {  // wave-uniform: a new (channel chunk, branch) pair
-                cur_pair = pr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = CK * cq + 8 * g + e;
-                    if (full)
-                        gb[e] = load4_unchecked(gn + (int64_t)((1 + b) * C + c) * HW + rowoff, w, aligned4, aligned4,
-                                                false);
-                    else
-                        gb[e] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, w, W, c < C,
-                                          aligned4);
-                }
-            }
-            const int ki = t / K;
-            const int kj = t - ki * K;
-            const int hh = h + (ki - r) * D;
-            const int dc = (kj - r) * D;
-            const bool hok = hh >= 0 && hh < H;
-            uint16_t bv[4][8];
-            uint16_t av[MB][8];
-            if (full && hok && w0 + dc - (dc & 1) >= 0 && w0 + kCols - 1 + dc < W) {  // wave-uniform
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = CK * cq + 8 * g + e;
-                    const f32x4 xs = load4_unchecked(xn + (int64_t)c * HW + (int64_t)hh * W, w + dc,
-                                                     aligned4 && ((dc & 3) == 0), aligned4, (dc & 1) != 0);
-#pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
-                    const T *wrow = wg + ((int64_t)(b * C + c) * KK + t) * C + cm0 + j;
-#pragma unroll
-                    for (int m = 0; m < MB; ++m) av[m][e] = wrow[16 * m];
-                }
-            } else
+            f32x4 gb[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int c = CK * cq + 8 * g + e;
-                const bool c_ok = c < C;
-                const f32x4 xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(hok ? hh : 0) * W, w + dc, W,
-                                           c_ok && hok, aligned4 && ((dc & 3) == 0));
+                if (full)
+                    gb[e] = load4_unchecked(gn + (int64_t)((1 + b) * C + c) * HW + rowoff, w, aligned4, aligned4,
+                                            false);
+                else
+                    gb[e] = load4_row(gn + (int64_t)((1 + b) * C + (c < C ? c : 0)) * HW + rowoff, w, W, c < C,
+                                      aligned4);
+            }
+            const int ta = max(i0 - p * KK, 0), tb = min(i1 - p * KK, KK);
+#pragma unroll 1
+            for (int t = ta; t < tb; ++t) {
+                const int ki = t / K;
+                const int kj = t - ki * K;
+                const int hh = h + (ki - r) * D;
+                const int dc = (kj - r) * D;
+                const bool hok = hh >= 0 && hh < H;
+                uint16_t bv[4][8];
+                uint16_t av[MB][8];
+                if (full && hok && w0 + dc - (dc & 1) >= 0 && w0 + kCols - 1 + dc < W) {  // wave-uniform
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
-                const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+                    for (int e = 0; e < 8; ++e) {
+                        const int c = CK * cq + 8 * g + e;
+                        const f32x4 xs = load4_unchecked(xn + (int64_t)c * HW + (int64_t)hh * W, w + dc,
+                                                         aligned4 && ((dc & 3) == 0), aligned4, (dc & 1) != 0);
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
+                        const T *wrow = wg + ((int64_t)(b * C + c) * KK + t) * C + cm0 + j;
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) av[m][e] = wrow[16 * m];
+                    }
+                } else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = CK * cq + 8 * g + e;
+                    const bool c_ok = c < C;
+                    const f32x4 xs = load4_row(xn + (int64_t)(c_ok ? c : 0) * HW + (int64_t)(hok ? hh : 0) * W,
+                                               w + dc, W, c_ok && hok, aligned4 && ((dc & 3) == 0));
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) bv[pb][e] = f32_to_bf16_bits(gb[e][pb] * xs[pb]);
+                    const T *wrow = wg + ((int64_t)(b * C + (c_ok ? c : 0)) * KK + t) * C;
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) {
+                        const int cp = cm0 + 16 * m + j;
+                        av[m][e] = (c_ok && cp < C) ? wrow[cp] : (uint16_t)0;
+                    }
+                }
+                bf16x8 bq[4];
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) bq[pb] = pack_bf16x8(bv[pb]);
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    const int cp = cm0 + 16 * m + j;
-                    av[m][e] = (c_ok && cp < C) ? wrow[cp] : (uint16_t)0;
+                    const bf16x8 aq = pack_bf16x8(av[m]);
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x32_bf16(aq, bq[pb], acc[m][pb]);
                 }
-            }
-            bf16x8 bq[4];
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) bq[pb] = pack_bf16x8(bv[pb]);
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                const bf16x8 aq = pack_bf16x8(av[m]);
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x32_bf16(aq, bq[pb], acc[m][pb]);
             }
         }
     }
