@@ -167,8 +167,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the DDPM hot path here is built and timed on a "
-              "single MI355X (--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU only: the DDPM hot path is timed on a single MI355X "
+              "(--gpus 1); it has no multi-GPU mode (each GPU would run its own share of the batch).",
+              file=sys.stderr)
         sys.exit(2)
 
     import dynamic_dilated_depthwise_amd as ddpm
