@@ -120,10 +120,14 @@ __global__ __launch_bounds__(64 * NW, NW == 16 ? 4 : (NW == 4 ? 2 : 1)) void bwd
                         a[m] = (c_ok && cp < C) ? wb[t * C + cp] : 0.f;
                     }
                 }
+                // raised issue priority while this wave's MFMAs go out, so that waves doing
+                // their address arithmetic do not hold the matrix pipe idle
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
                     for (int pb = 0; pb < 4; ++pb) acc[m][pb] = mfma_16x16x4_f32(a[m], gb[pb] * xs[pb], acc[m][pb]);
+                __builtin_amdgcn_s_setprio(0);
             }
         }
     } else {
