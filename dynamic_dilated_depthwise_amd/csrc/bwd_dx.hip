@@ -367,6 +367,9 @@ __global__ __launch_bounds__(256 * NG, NG == 4 ? 4 : (NG == 1 ? 2 : 1)) void bwd
                     load_G(combo, gcur);
                     load_bias(combo, bcur);
                 }
+                // one wave group: raised issue priority while the stage's MFMAs go out
+                // (with two or four lockstep groups it measured slower)
+                if constexpr (NG == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int u = 0; u < S::SUB; ++u) {
                     if (FULLW) {
@@ -389,6 +392,7 @@ __global__ __launch_bounds__(256 * NG, NG == 4 ? 4 : (NG == 1 ? 2 : 1)) void bwd
                         if (in_stage || more) acur[0] = an;
                     }
                 }
+                if constexpr (NG == 1) __builtin_amdgcn_s_setprio(0);
             }
             if (last) {
                 // the bias is in the fp32 sum before the tap's single rounding
