@@ -26,16 +26,19 @@ __all__ = [
     "ddpm_filter_bwd",
     "ddpm_fused_fwd",
     "ddpm_fused_bwd",
+    "ddpm_fused_bwd_noalloc",
     "ddpm_reduce_partials",
     "ddpm_status_string",
     "num_partials_for",
     "library_path",
     "MAX_PARTIALS",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libddpm.so")
 MAX_PARTIALS = 16
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # the library's fixed partials buffer (DDPM_NOALLOC_SCRATCH_BYTES)
 _CUS = 256  # compute units of the chip (MI355X)
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -69,7 +72,9 @@ def _load():
     lib.ddpm_fused_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I, I, P]
     lib.ddpm_fused_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I64, I64, I64, I64, I, I, P]
     lib.ddpm_reduce_partials.argtypes = [P, P, I, P, P, I64, I, I, P]
-    for f in ("ddpm_filter_fwd", "ddpm_filter_bwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials"):
+    lib.ddpm_fused_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I64, I64, I64, I64, I, I, P]
+    for f in ("ddpm_filter_fwd", "ddpm_filter_bwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials",
+              "ddpm_fused_bwd_noalloc"):
         getattr(lib, f).restype = I
     lib.ddpm_status_string.argtypes = [I]
     lib.ddpm_status_string.restype = ctypes.c_char_p
@@ -203,3 +208,27 @@ def ddpm_reduce_partials(dweight_partials, dbias_partials, grad_weight, grad_bia
     outs = (_dev(grad_weight, "grad_weight", dt, (R, C)), _dev(grad_bias, "grad_bias", dt, (R,)))
     _check("ddpm_reduce_partials",
            _load().ddpm_reduce_partials(*args, S, *outs, C, K, _dtype_code(grad_weight), _stream(stream)))
+
+
+def ddpm_fused_bwd_noalloc(x, y, weight, bias, grad_out, grad_x, grad_y, grad_weight, grad_bias, K,
+                           num_partials=None, stream=None):
+    """grad_x, grad_y, grad_weight and grad_bias with the float32 partials kept in the
+    library's fixed device buffer: no workspace, nothing allocated (see include/ddpm.h).
+
+    grad_x or grad_y may be None; grad_weight and grad_bias are both given or both
+    None.  num_partials defaults to num_partials_for(N, C, H, W, K)."""
+    N, C, H, W = x.shape
+    R = 3 * C * K * K
+    dt = x.dtype
+    if (grad_weight is None) != (grad_bias is None):
+        raise ValueError("grad_weight and grad_bias must both be given or both be None")
+    S = num_partials_for(N, C, H, W, K) if num_partials is None else int(num_partials)
+    null = ctypes.c_void_p(None)
+    args = (_dev(x, "x", dt), _dev(y, "y", dt, (N, C, H, W)), _dev(weight, "weight", dt, (R, C)),
+            _dev(bias, "bias", dt, (R,)), _dev(grad_out, "grad_out", dt, (N, 4 * C, H, W)),
+            null if grad_x is None else _dev(grad_x, "grad_x", dt, (N, C, H, W)),
+            null if grad_y is None else _dev(grad_y, "grad_y", dt, (N, C, H, W)),
+            null if grad_weight is None else _dev(grad_weight, "grad_weight", dt, (R, C)),
+            null if grad_bias is None else _dev(grad_bias, "grad_bias", dt, (R,)))
+    _check("ddpm_fused_bwd_noalloc",
+           _load().ddpm_fused_bwd_noalloc(*args, S, N, C, H, W, K, _dtype_code(x), _stream(stream)))

@@ -3,10 +3,38 @@
 // enqueued, so a rejected call has no effect.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/ddpm.h"
 #include "launchers.hpp"
 
+// Device memory of ddpm_fused_bwd_noalloc: the float32 weight/bias partials live
+// here instead of in a caller workspace.  Every GPU the library runs on holds its
+// own copy (loaded with the code object) until the process ends.  In host code the
+// name is only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, once per device (scratch_of_current_device).
+static __device__ __align__(256) float scratch[DDPM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first call
+// made with that device current and kept.  DDPM_OK or DDPM_ERR_HIP.
+int scratch_of_current_device(float **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DDPM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DDPM_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<float *>(g_scratch_ptr[dev]);
+    return DDPM_OK;
+}
 
 bool bad_ptr(const void *p, int dtype) {
     if (p == nullptr) return true;
@@ -53,6 +81,7 @@ const char *ddpm_status_string(int status) {
         case DDPM_ERR_INVALID_ARG: return "DDPM_ERR_INVALID_ARG";
         case DDPM_ERR_UNSUPPORTED: return "DDPM_ERR_UNSUPPORTED";
         case DDPM_ERR_HIP: return "DDPM_ERR_HIP";
+        case DDPM_ERR_SCRATCH_LIMIT: return "DDPM_ERR_SCRATCH_LIMIT";
         default: return "DDPM_ERR_UNKNOWN";
     }
 }
@@ -140,9 +169,16 @@ int ddpm_fused_fwd(const void *x, const void *y, const void *weight, const void 
                                             dtype == DDPM_BF16, al, stream));
 }
 
-int ddpm_fused_bwd(const void *x, const void *y, const void *weight, const void *bias, const void *grad_out,
-                   void *grad_x, void *grad_y, float *dweight_partials, float *dbias_partials, int num_partials,
-                   int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by ddpm_fused_bwd and ddpm_fused_bwd_noalloc: the inputs, the
+// requested outputs (want_dw: the partials, of pwb / pbb bytes, are written) and
+// their overlaps.  `al` receives the kernels' 16-byte alignment flag.
+int check_fused_bwd(const void *x, const void *y, const void *weight, const void *bias, const void *grad_out,
+                    void *grad_x, void *grad_y, void *out3, void *out4, int64_t b3, int64_t b4, bool want_dw,
+                    int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype, bool *al) {
     int st = check_shape(N, C, H, W, K, dtype);
     if (st != DDPM_OK) return st;
     if (bad_ptr(x, dtype) || bad_ptr(y, dtype) || bad_ptr(weight, dtype) || bad_ptr(bias, dtype) ||
@@ -150,23 +186,16 @@ int ddpm_fused_bwd(const void *x, const void *y, const void *weight, const void 
         return DDPM_ERR_INVALID_ARG;
     const bool want_dx = grad_x != nullptr;
     const bool want_dy = grad_y != nullptr;
-    if ((dweight_partials == nullptr) != (dbias_partials == nullptr)) return DDPM_ERR_INVALID_ARG;
-    const bool want_dw = dweight_partials != nullptr;
     if (!want_dx && !want_dy && !want_dw) return DDPM_ERR_INVALID_ARG;
-    if ((want_dx && bad_ptr(grad_x, dtype)) || (want_dy && bad_ptr(grad_y, dtype)) ||
-        (want_dw && (bad_ptr(dweight_partials, DDPM_F32) || bad_ptr(dbias_partials, DDPM_F32))))
-        return DDPM_ERR_INVALID_ARG;
-    if (want_dw && (num_partials < 1 || num_partials > DDPM_MAX_PARTIALS)) return DDPM_ERR_INVALID_ARG;
+    if ((want_dx && bad_ptr(grad_x, dtype)) || (want_dy && bad_ptr(grad_y, dtype))) return DDPM_ERR_INVALID_ARG;
     const int64_t es = dtype == DDPM_BF16 ? 2 : 4;
     const int64_t HW = H * W;
     const int64_t R = 3 * C * K * K;
     const int64_t xb = N * C * HW * es, gb = N * 4 * C * HW * es;
-    const int64_t S = want_dw ? num_partials : 0;
-    const int64_t pwb = S * R * C * 4, pbb = S * R * 4;
     const void *ins[5] = {x, y, weight, bias, grad_out};
     const int64_t inb[5] = {xb, xb, R * C * es, R * es, gb};
-    void *outs[4] = {grad_x, grad_y, dweight_partials, dbias_partials};
-    const int64_t outb[4] = {xb, xb, pwb, pbb};
+    void *outs[4] = {grad_x, grad_y, want_dw ? out3 : nullptr, want_dw ? out4 : nullptr};
+    const int64_t outb[4] = {xb, xb, b3, b4};
     for (int o = 0; o < 4; ++o) {
         if (outs[o] == nullptr) continue;
         for (int i = 0; i < 5; ++i)
@@ -174,12 +203,73 @@ int ddpm_fused_bwd(const void *x, const void *y, const void *weight, const void 
         for (int p = o + 1; p < 4; ++p)
             if (outs[p] != nullptr && overlaps(outs[o], outb[o], outs[p], outb[p])) return DDPM_ERR_INVALID_ARG;
     }
-    const bool al = (W % 4) == 0 && aligned16(x) && aligned16(y) && aligned16(weight) && aligned16(grad_out) &&
-                    (!want_dx || aligned16(grad_x)) && (!want_dy || aligned16(grad_y));
+    *al = (W % 4) == 0 && aligned16(x) && aligned16(y) && aligned16(weight) && aligned16(grad_out) &&
+          (!want_dx || aligned16(grad_x)) && (!want_dy || aligned16(grad_y));
+    return DDPM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ddpm_fused_bwd(const void *x, const void *y, const void *weight, const void *bias, const void *grad_out,
+                   void *grad_x, void *grad_y, float *dweight_partials, float *dbias_partials, int num_partials,
+                   int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype, hipStream_t stream) {
+    if ((dweight_partials == nullptr) != (dbias_partials == nullptr)) return DDPM_ERR_INVALID_ARG;
+    const bool want_dw = dweight_partials != nullptr;
+    if (want_dw && (bad_ptr(dweight_partials, DDPM_F32) || bad_ptr(dbias_partials, DDPM_F32)))
+        return DDPM_ERR_INVALID_ARG;
+    if (want_dw && (num_partials < 1 || num_partials > DDPM_MAX_PARTIALS)) return DDPM_ERR_INVALID_ARG;
+    const int64_t R = 3 * C * K * K;
+    const int64_t S = want_dw ? num_partials : 0;
+    bool al = false;
+    const int st = check_fused_bwd(x, y, weight, bias, grad_out, grad_x, grad_y, dweight_partials, dbias_partials,
+                                   S * R * C * 4, S * R * 4, want_dw, N, C, H, W, K, dtype, &al);
+    if (st != DDPM_OK) return st;
     (void)hipGetLastError();
     return status_of(ddpm::launch_fused_bwd(x, y, weight, bias, grad_out, grad_x, grad_y, dweight_partials,
                                             dbias_partials, want_dw ? num_partials : 1, (int)N, (int)C, (int)H,
                                             (int)W, K, dtype == DDPM_BF16, al, stream));
+}
+
+int ddpm_fused_bwd_noalloc(const void *x, const void *y, const void *weight, const void *bias, const void *grad_out,
+                           void *grad_x, void *grad_y, void *grad_weight, void *grad_bias, int num_partials,
+                           int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype, hipStream_t stream) {
+    if ((grad_weight == nullptr) != (grad_bias == nullptr)) return DDPM_ERR_INVALID_ARG;
+    const bool want_dw = grad_weight != nullptr;
+    if (want_dw && (bad_ptr(grad_weight, dtype) || bad_ptr(grad_bias, dtype))) return DDPM_ERR_INVALID_ARG;
+    if (want_dw && (num_partials < 1 || num_partials > DDPM_MAX_PARTIALS)) return DDPM_ERR_INVALID_ARG;
+    const int64_t es = dtype == DDPM_BF16 ? 2 : 4;
+    const int64_t R = 3 * C * K * K;
+    bool al = false;
+    int st = check_fused_bwd(x, y, weight, bias, grad_out, grad_x, grad_y, grad_weight, grad_bias, R * C * es,
+                             R * es, want_dw, N, C, H, W, K, dtype, &al);
+    if (st != DDPM_OK) return st;
+    // Partials of the weight at float 0, of the bias at the next 256-byte boundary.
+    const int64_t S = want_dw ? num_partials : 0;
+    const int64_t bias_off = (S * R * C + 63) / 64 * 64;
+    if (want_dw && (bias_off + S * R) * (int64_t)sizeof(float) > (int64_t)DDPM_NOALLOC_SCRATCH_BYTES)
+        return DDPM_ERR_SCRATCH_LIMIT;
+    if (stream != nullptr && stream != hipStreamPerThread) {
+        int cur = -1, sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) return DDPM_ERR_HIP;
+        if (cur != sdev) return DDPM_ERR_INVALID_ARG;
+    }
+    float *pw = nullptr, *pb = nullptr;
+    if (want_dw) {
+        float *base = nullptr;
+        st = scratch_of_current_device(&base);
+        if (st != DDPM_OK) return st;
+        pw = base;
+        pb = base + bias_off;
+    }
+    (void)hipGetLastError();
+    st = status_of(ddpm::launch_fused_bwd(x, y, weight, bias, grad_out, grad_x, grad_y, pw, pb,
+                                          want_dw ? num_partials : 1, (int)N, (int)C, (int)H, (int)W, K,
+                                          dtype == DDPM_BF16, al, stream));
+    if (st != DDPM_OK || !want_dw) return st;
+    return status_of(ddpm::launch_reduce_partials(pw, pb, num_partials, grad_weight, grad_bias, R, (int)C,
+                                                  dtype == DDPM_BF16, stream));
 }
 
 int ddpm_reduce_partials(const float *dweight_partials, const float *dbias_partials, int num_partials,

@@ -24,7 +24,8 @@
  *   [3*C*K*K, C]; bias is [3*C*K*K]; taps is [N, 3*C*K*K, H, W]; out and
  *   grad_out are [N, 4*C, H, W].  Tensors are in `dtype` unless stated; the
  *   weight-gradient partials are always float32.  The library never allocates,
- *   frees or synchronises; it keeps no state between calls.  Outputs must not
+ *   frees or synchronises; apart from the fixed device buffer of
+ *   ddpm_fused_bwd_noalloc it keeps no state between calls.  Outputs must not
  *   overlap inputs or each other.  Every output element is written exactly once
  *   (nothing is accumulated into), so outputs need no zeroing.
  * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
@@ -46,7 +47,9 @@
  *                           num_partials outside [1, DDPM_MAX_PARTIALS];
  *     DDPM_ERR_UNSUPPORTED  K not in {1, 3, 5} (the dilation set is fixed), or a
  *                           shape whose grid exceeds 2^31 - 1 workgroups;
- *     DDPM_ERR_HIP          a HIP launch or attribute call failed.
+ *     DDPM_ERR_HIP          a HIP launch or attribute call failed;
+ *     DDPM_ERR_SCRATCH_LIMIT (ddpm_fused_bwd_noalloc only) the partials do not
+ *                           fit the library's fixed device buffer.
  *   No C++ exception crosses this interface.  Calls are re-entrant and
  *   thread-safe.
  */
@@ -66,7 +69,8 @@ typedef enum {
     DDPM_OK = 0,
     DDPM_ERR_INVALID_ARG = -1,
     DDPM_ERR_UNSUPPORTED = -2,
-    DDPM_ERR_HIP = -3
+    DDPM_ERR_HIP = -3,
+    DDPM_ERR_SCRATCH_LIMIT = -4
 } ddpm_status;
 
 /* Largest depthwise channel count accepted. */
@@ -168,6 +172,40 @@ int ddpm_fused_bwd(const void *x, const void *y, const void *weight, const void 
 int ddpm_reduce_partials(const float *dweight_partials, const float *dbias_partials,
                          int num_partials, void *grad_weight, void *grad_bias,
                          int64_t C, int K, int dtype, hipStream_t stream);
+
+/* Size of the device buffer inside the library that ddpm_fused_bwd_noalloc keeps its
+ * partials in (one per GPU, held until the process ends). */
+#define DDPM_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/*
+ * ddpm_fused_bwd_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ddpm_fused_bwd followed by ddpm_reduce_partials, with the float32 partials kept
+ * in a fixed buffer inside the library instead of a caller workspace.  The call
+ * allocates and frees nothing and calls no allocating routine.
+ *
+ *   x, y, weight, bias, grad_out, grad_x, grad_y   as for ddpm_fused_bwd
+ *   grad_weight [3*C*K*K, C]   out  dtype
+ *   grad_bias   [3*C*K*K]      out  dtype
+ *   num_partials in [1, DDPM_MAX_PARTIALS]: the token split, as for ddpm_fused_bwd.
+ * The results equal those of ddpm_fused_bwd + ddpm_reduce_partials with the same
+ * num_partials.  grad_x or grad_y may be NULL (skipped); grad_weight and grad_bias
+ * are both NULL (skipped, num_partials ignored) or both non-NULL.
+ * Limit: the partials take num_partials * (3*C*K*K*C + 3*C*K*K) floats (plus at
+ * most 63 floats of alignment) of the DDPM_NOALLOC_SCRATCH_BYTES buffer; a larger
+ * request returns DDPM_ERR_SCRATCH_LIMIT before anything is enqueued (C = 64 fits
+ * up to K = 5 with 16 partials; use fewer partials or ddpm_fused_bwd beyond it).
+ * `stream` must belong to the current device (else DDPM_ERR_INVALID_ARG).
+ * Sharing: every call on one GPU uses that GPU's one buffer, so calls that may run
+ * at the same time on one GPU (different streams, or host threads) race and give
+ * wrong gradients; order them on one stream.  Each call writes every partial it
+ * later reads, so nothing needs clearing between calls.
+ */
+int ddpm_fused_bwd_noalloc(const void *x, const void *y, const void *weight, const void *bias,
+                           const void *grad_out, void *grad_x, void *grad_y,
+                           void *grad_weight, void *grad_bias, int num_partials,
+                           int64_t N, int64_t C, int64_t H, int64_t W, int K, int dtype,
+                           hipStream_t stream);
 
 /* Static, human-readable name of a ddpm_status value. */
 const char *ddpm_status_string(int status);

@@ -16,7 +16,7 @@ import dynamic_dilated_depthwise_amd as ddpm
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ddpm.h")
 
-OK, INVALID, UNSUPPORTED, HIPERR = 0, -1, -2, -3
+OK, INVALID, UNSUPPORTED, HIPERR, SCRATCH = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 
 
@@ -37,7 +37,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "ddpm_filter_fwd", "ddpm_filter_bwd", "ddpm_fused_fwd", "ddpm_fused_bwd", "ddpm_reduce_partials",
-        "ddpm_status_string"])
+        "ddpm_fused_bwd_noalloc", "ddpm_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -50,6 +50,7 @@ def test_status_strings(lib):
     assert ddpm.ddpm_status_string(INVALID) == "DDPM_ERR_INVALID_ARG"
     assert ddpm.ddpm_status_string(UNSUPPORTED) == "DDPM_ERR_UNSUPPORTED"
     assert ddpm.ddpm_status_string(HIPERR) == "DDPM_ERR_HIP"
+    assert ddpm.ddpm_status_string(SCRATCH) == "DDPM_ERR_SCRATCH_LIMIT"
 
 
 # Fake, well-aligned, non-overlapping "device" addresses; never dereferenced because
@@ -81,11 +82,15 @@ def _bwd(lib, x=A, y=B, w=Cp, b=D, g=E, gx=F, gy=G, pw=Hp, pb=Ip, S=1, N=1, C=8,
     return lib.ddpm_fused_bwd(x, y, w, b, g, gx, gy, pw, pb, S, N, C, H, W, K, dt, None)
 
 
+def _noalloc(lib, x=A, y=B, w=Cp, b=D, g=E, gx=F, gy=G, gw=Hp, gb=Ip, S=1, N=1, C=8, H=16, W=16, K=3, dt=F32):
+    return lib.ddpm_fused_bwd_noalloc(x, y, w, b, g, gx, gy, gw, gb, S, N, C, H, W, K, dt, None)
+
+
 def _reduce(lib, pw=A, pb=B, S=1, gw=Cp, gb=D, C=8, K=3, dt=F32):
     return lib.ddpm_reduce_partials(pw, pb, S, gw, gb, C, K, dt, None)
 
 
-@pytest.mark.parametrize("call", [_filter, _filter_bwd, _fused, _bwd])
+@pytest.mark.parametrize("call", [_filter, _filter_bwd, _fused, _bwd, _noalloc])
 def test_shape_validation(lib, call):
     for kw in (dict(N=0), dict(C=0), dict(H=0), dict(W=-1), dict(C=4096), dict(dt=2), dict(dt=-1),
                dict(H=1 << 16, W=1 << 15)):
@@ -120,6 +125,22 @@ def test_partial_count_validation(lib):
         # with no partials requested the count is not used (checked on a call
         # that still fails validation, so nothing is launched)
         assert _bwd(lib, S=S, pw=0, pb=0, K=2) == UNSUPPORTED
+
+
+def test_noalloc_validation(lib):
+    for name in ("x", "y", "w", "b", "g", "gw", "gb"):
+        assert _noalloc(lib, **{name: 0}) == INVALID       # gw / gb alone: both or neither
+    assert _noalloc(lib, gx=0, gy=0, gw=0, gb=0) == INVALID  # nothing requested
+    assert _noalloc(lib, gw=Hp + 1, dt=BF16) == INVALID     # misaligned gradient
+    for S in (0, -1, 17):
+        assert _noalloc(lib, S=S) == INVALID
+    assert _noalloc(lib, gw=A) == INVALID                  # overlaps x
+    # the partials beyond the fixed buffer: C=128, K=5, 16 partials need 79 MB
+    assert _noalloc(lib, C=128, K=5, S=16) == SCRATCH
+    # C=64, K=5, 16 partials (20 MB) fit: such a call passes validation (not made
+    # here, it would launch); with fewer partials C=128, K=5 fits as well
+    assert 16 * (4800 * 64 + 4800) * 4 <= ddpm.NOALLOC_SCRATCH_BYTES
+    assert 6 * (9600 * 128 + 9600) * 4 <= ddpm.NOALLOC_SCRATCH_BYTES
 
 
 def test_reduce_shape_validation(lib):
