@@ -1,7 +1,7 @@
 """Benchmark of the DDPM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--dtype f32|bf16]
-                    [--workload target_256] [--no-cpu-baseline]
+                    [--workload target_256] [--no-cpu-baseline] [--no-bf16]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 (B=1, C=64, K=3, 256x256 by default):
@@ -19,7 +19,10 @@ the timed region.  All inputs are resident in HBM before timing starts.
 
 After the steps every kernel is also launched alone, each time right after a 1 GiB
 read that flushes L2 and the MALL ("cold": median, p10, p90), and a 1 GiB device
-copy gives the attainable-bandwidth ceiling.
+copy gives the attainable-bandwidth ceiling.  With --dtype f32 (the default) the
+same measurement is then made for bfloat16 and carried as the line's "bf16"
+object (its own steps, per-kernel figures, cold filter TB/s and roofline);
+``value`` and ``dtype`` stay those of float32.
 
 Printed on stdout: ONE JSON line.  ``value`` is the filter's effective bandwidth
 in TB/s (algorithmic bytes / cold median filter duration; the warm in-step figure
@@ -121,68 +124,55 @@ def recorded_traffic(name, workload, dtype):
     return None
 
 
-def run_cpu_baseline(h, shape, budget_s=10.0):
-    """The fp64 oracle on the same inputs: full steps (filter, fused forward, fused
-    backward) repeated until about budget_s of host time is spent; per-part means."""
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (or the platform string)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def run_cpu_baseline(h, shape, reps=3):
+    """The fp64 oracle on the same inputs: one warm-up step (filter, fused forward,
+    fused backward), then `reps` timed steps; per-part medians."""
     import oracle
     orc = oracle.default()
     a = {k: v.double().numpy() for k, v in h.items()}
     K = shape.K
-    t = {"filter": 0.0, "fused_fwd": 0.0, "fused_bwd": 0.0}
-    reps = 0
+    parts = {
+        "filter": lambda: orc.filter_fwd(a["x"], a["taps"], K),
+        "fused_fwd": lambda: orc.fused_fwd(a["x"], a["y"], a["weight"], a["bias"], K),
+        "fused_bwd": lambda: orc.fused_bwd(a["x"], a["y"], a["weight"], a["bias"], a["grad_out"], K),
+    }
+    t = {k: [] for k in parts}
     start = time.perf_counter()
-    while reps == 0 or time.perf_counter() - start < budget_s:
-        t0 = time.perf_counter()
-        orc.filter_fwd(a["x"], a["taps"], K)
-        t1 = time.perf_counter()
-        orc.fused_fwd(a["x"], a["y"], a["weight"], a["bias"], K)
-        t2 = time.perf_counter()
-        orc.fused_bwd(a["x"], a["y"], a["weight"], a["bias"], a["grad_out"], K)
-        t3 = time.perf_counter()
-        t["filter"] += t1 - t0
-        t["fused_fwd"] += t2 - t1
-        t["fused_bwd"] += t3 - t2
-        reps += 1
-    out = {k: v / reps for k, v in t.items()}
+    for rep in range(reps + 1):
+        for name, fn in parts.items():
+            t0 = time.perf_counter()
+            fn()
+            if rep > 0:  # rep 0 is the warm-up
+                t[name].append(time.perf_counter() - t0)
+    out = {k: sorted(v)[len(v) // 2] for k, v in t.items()}
     out["reps"] = reps
     out["total_s"] = time.perf_counter() - start
     return out
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--dtype", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--workload", default="target_256")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration-mib", type=int, default=1024,
-                    help="before the steps, time a plain device-to-device copy of this many MiB "
-                         "(a known-size kernel for scaling HBM counters, and the attainable-bandwidth ceiling); "
-                         "0 skips it")
-    ap.add_argument("--cold-reps", type=int, default=20,
-                    help="after the steps, time each kernel this many times alone, each after a read of "
-                         "a 1 GiB buffer that evicts L2 and the MALL (0 skips it)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the DDPM hot path is timed on a single MI355X "
-              "(--gpus 1); it has no multi-GPU mode (each GPU would run its own share of the batch).",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import dynamic_dilated_depthwise_amd as ddpm
-    from dynamic_dilated_depthwise_amd import synth
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dtype = torch.float32 if args.dtype == "f32" else torch.bfloat16
-    es = 4 if args.dtype == "f32" else 2
+def measure(args, ddpm, synth, dt_name, log_prefix=""):
+    """Time one dtype of the workload: the in-step per-kernel means over
+    args.steps whole steps, the materialised backward beside them, and the cold
+    launches.  Returns the measurements and the seeded host inputs."""
+    dtype = torch.float32 if dt_name == "f32" else torch.bfloat16
+    es = 4 if dt_name == "f32" else 2
     shape, block = synth.WORKLOADS[args.workload]
     N, C, H, W, K = shape.N, shape.C, shape.H, shape.W, shape.K
     R = shape.R
     S = ddpm.num_partials_for(N, C, H, W, K)
-    log(f"workload {args.workload} N={N} C={C} H={H} W={W} K={K} dtype={args.dtype} S={S}")
+    log(f"{log_prefix}workload {args.workload} N={N} C={C} H={H} W={W} K={K} dtype={dt_name} S={S}")
 
     h = synth.make_inputs(shape, block, dtype, taps=True, grad=True)
     d = {k: v.to("cuda").contiguous() for k, v in h.items()}
@@ -223,26 +213,7 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    copy_cal = None
-    if args.copy_calibration_mib > 0:
-        nbytes = args.copy_calibration_mib * (1 << 20)
-        src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
-        dst = torch.empty_like(src)
-        times = []
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            dst.copy_(src)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = sorted(times)[len(times) // 2]
-        copy_cal = {"bytes_read": nbytes, "bytes_written": nbytes, "median_ms": round(ms, 5),
-                    "GB_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
-        log(f"copy calibration {copy_cal}")
-        del src, dst
-
-    log(f"warmup {args.warmup} steps")
+    log(f"{log_prefix}warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -250,7 +221,7 @@ def main():
     # Timed region: K whole steps, events around every call on the launch stream.
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in calls]
           for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
+    log(f"{log_prefix}timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -260,7 +231,7 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     per = {name: sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)) / args.steps
            for i, (name, _) in enumerate(calls)}
-    log("per-call ms " + " ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    log(f"{log_prefix}per-call ms " + " ".join(f"{k}={v:.4f}" for k, v in per.items()))
 
     for name, fn in extra_calls:
         for _ in range(args.warmup):
@@ -274,7 +245,7 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         per[name] = sum(e0.elapsed_time(e1) for e0, e1 in xev) / args.steps
-        log(f"{name} (outside the step) ms={per[name]:.4f}")
+        log(f"{log_prefix}{name} (outside the step) ms={per[name]:.4f}")
 
     # Cold launches: each kernel alone after a 1 GiB read that evicts L2 and the MALL
     # with clean lines, so its inputs come from HBM and no write-back of the flush
@@ -297,10 +268,10 @@ def main():
             q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
             cold[name] = {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
         del flush, sink
-        log("cold median ms " + " ".join(f"{k}={v['median']:.4f}" for k, v in cold.items()))
+        log(f"{log_prefix}cold median ms " + " ".join(f"{k}={v['median']:.4f}" for k, v in cold.items()))
 
     alg = algorithmic(shape, es, S)
-    peak_t = MFMA_PEAK_TFLOPS[args.dtype]
+    peak_t = MFMA_PEAK_TFLOPS[dt_name]
     kernels = {}
     for name, ms in per.items():
         a = alg[name]
@@ -322,7 +293,7 @@ def main():
 
     dom = max((n for n, _ in calls if n != "reduce"), key=lambda n: per[n])
     kd = kernels[dom]
-    traffic = recorded_traffic(dom, args.workload, args.dtype)
+    traffic = recorded_traffic(dom, args.workload, dt_name)
     if kd["bound"] == "hbm":
         roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": kd["frac"], "traffic": traffic}
@@ -330,43 +301,133 @@ def main():
         roofline = {"kernel": dom, "bound": "mfma", "achieved": kd["TFLOP_s"], "peak": peak_t, "unit": "TFLOP/s",
                     "frac": kd["frac"], "traffic": traffic}
     for name in kernels:
-        kernels[name]["hbm_traffic_bytes"] = recorded_traffic(name, args.workload, args.dtype)
+        kernels[name]["hbm_traffic_bytes"] = recorded_traffic(name, args.workload, dt_name)
 
     filter_warm_tbs = kernels["filter"]["GB_s"] / 1e3
     if "filter" in cold:
         filter_tbs = alg["filter"]["bytes"] / (cold["filter"]["median"] * 1e-3) / 1e12
-        value_timing = f"median of {args.cold_reps} single filter launches, each after a 1 GiB read that flushes L2 and MALL"
+        value_timing = (f"median of {args.cold_reps} single filter launches, each after a 1 GiB read that "
+                        "flushes L2 and MALL")
     else:
         filter_tbs = filter_warm_tbs
         value_timing = "mean filter launch inside the timed steps (warm)"
     fwd_ms = per["fused_fwd"]
     fwd_bwd_ms = per["fused_fwd"] + per["bwd_dx"] + per["bwd_dy"] + per["bwd_dw"] + per["reduce"]
     gen_tflops = alg["fused_fwd"]["flops"] / (fwd_ms * 1e-3) / 1e12
+    res = {
+        "dtype": dt_name, "shape": shape, "S": S, "h": h, "alg": alg, "ms_per_step": ms_per_step,
+        "value_timing": value_timing, "filter_tbs": filter_tbs, "filter_warm_tbs": filter_warm_tbs,
+        "filter_ms": per["filter"], "fwd_ms": fwd_ms, "fwd_bwd_ms": fwd_bwd_ms, "gen_tflops": gen_tflops,
+        "peak_t": peak_t, "kernels": kernels, "roofline": roofline,
+    }
+    del d, out_f, out, gx, gy, pw, pb, gw, gb, gx_f, gk_f
+    torch.cuda.empty_cache()
+    return res
+
+
+def summary(m):
+    """The per-dtype figures carried on the JSON line."""
+    return {
+        "value_TB_s": round(m["filter_tbs"], 4),
+        "value_timing": m["value_timing"],
+        "ms_per_step": round(m["ms_per_step"], 4),
+        "filter_warm_TB_s": round(m["filter_warm_tbs"], 4),
+        "filter_ms": round(m["filter_ms"], 5),
+        "filter_hbm_frac": round(m["filter_tbs"] * 1e3 / HBM_PEAK_GBS, 4),
+        "filter_warm_hbm_frac": m["kernels"]["filter"]["frac"],
+        "fused_fwd_ms": round(m["fwd_ms"], 5),
+        "fused_fwd_bwd_ms": round(m["fwd_bwd_ms"], 5),
+        "fused_fwd_mfma_tflops": round(m["gen_tflops"], 2),
+        "fused_fwd_mfma_frac": round(m["gen_tflops"] / m["peak_t"], 4),
+        "kernels": m["kernels"],
+        "roofline": m["roofline"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--workload", default="target_256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="with --dtype f32, skip the bfloat16 step that is otherwise timed after the float32 one "
+                         "and carried as the line's \"bf16\" object")
+    ap.add_argument("--copy-calibration-mib", type=int, default=1024,
+                    help="before the steps, time a plain device-to-device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM counters, and the attainable-bandwidth ceiling); "
+                         "0 skips it")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="after the steps, time each kernel this many times alone, each after a read of "
+                         "a 1 GiB buffer that evicts L2 and the MALL (0 skips it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the DDPM hot path is timed on a single MI355X "
+              "(--gpus 1); it has no multi-GPU mode (each GPU would run its own share of the batch).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import dynamic_dilated_depthwise_amd as ddpm
+    from dynamic_dilated_depthwise_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    stream = torch.cuda.current_stream()
+
+    copy_cal = None
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        copy_cal = {"bytes_read": nbytes, "bytes_written": nbytes, "median_ms": round(ms, 5),
+                    "GB_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+        log(f"copy calibration {copy_cal}")
+        del src, dst
+
+    m = measure(args, ddpm, synth, args.dtype)
+    shape, S = m["shape"], m["S"]
+    N, C, H, W, K = shape.N, shape.C, shape.H, shape.W, shape.K
+    m_bf16 = None
+    if args.dtype == "f32" and not args.no_bf16:
+        m_bf16 = measure(args, ddpm, synth, "bf16", log_prefix="bf16: ")
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline: fp64 oracle, full steps on the host cores for about 10 s")
+        log("cpu baseline: fp64 oracle, one warm-up step then the median of 3 on the host cores")
         cores = len(os.sched_getaffinity(0))
         omp = os.environ.get("OMP_NUM_THREADS")
         threads = min(cores, int(omp)) if omp else cores
-        t = run_cpu_baseline(h, shape)
-        f_bytes = alg["filter"]["bytes"]
+        t = run_cpu_baseline(m["h"], shape)
+        f_bytes = m["alg"]["filter"]["bytes"]
         cpu = {"value": round(f_bytes / t["filter"] / 1e12, 5), "unit": "TB/s", "cores": threads, "kind": "oracle",
-               "sample": f"{t['reps']} full steps of the same {args.workload} workload (filter, fused fwd, "
-                         f"fused bwd) in fp64 on the host, {t['total_s']:.1f} s in all; value is the filter's "
-                         "algorithmic bytes / mean oracle filter time",
+               "sample": f"the same {args.workload} workload in fp64 on the host ({cpu_model()}): one warm-up "
+                         f"step (filter, fused fwd, fused bwd) then {t['reps']} timed steps, {t['total_s']:.1f} s "
+                         "in all; value is the filter's algorithmic bytes / median oracle filter time",
+               "cpu_model": cpu_model(),
                "filter_s": round(t["filter"], 4), "fused_fwd_s": round(t["fused_fwd"], 4),
                "fused_bwd_s": round(t["fused_bwd"], 4), "reps": t["reps"]}
         log(f"cpu baseline {cpu}")
 
+    sm = summary(m)
     line = {
         "metric": METRIC,
-        "value": round(filter_tbs, 4),
+        "value": sm.pop("value_TB_s"),
         "unit": "TB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": sm.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -375,19 +436,11 @@ def main():
         "config": {"workload": f"DDPM {args.workload}: B={N} C={C} K={K} {H}x{W}, "
                                "filter + fused fwd + fused bwd (dX, dY, dW partials) + reduce",
                    "N": N, "C": C, "H": H, "W": W, "K": K, "num_partials": S},
-        "value_timing": value_timing,
-        "filter_warm_TB_s": round(filter_warm_tbs, 4),
-        "filter_ms": round(per["filter"], 5),
-        "filter_hbm_frac": round(filter_tbs * 1e3 / HBM_PEAK_GBS, 4),
-        "filter_warm_hbm_frac": kernels["filter"]["frac"],
-        "fused_fwd_ms": round(fwd_ms, 5),
-        "fused_fwd_bwd_ms": round(fwd_bwd_ms, 5),
-        "fused_fwd_mfma_tflops": round(gen_tflops, 2),
-        "fused_fwd_mfma_frac": round(gen_tflops / peak_t, 4),
-        "kernels": kernels,
-        "roofline": roofline,
-        "cpu_baseline": cpu,
     }
+    line.update(sm)
+    line["cpu_baseline"] = cpu
+    if m_bf16 is not None:
+        line["bf16"] = summary(m_bf16)
     if copy_cal is not None:
         line["copy_calibration"] = copy_cal
     print(json.dumps(line), flush=True)
