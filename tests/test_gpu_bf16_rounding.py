@@ -8,6 +8,7 @@ bf16 values) or one fp32 addition in a fixed order, so a few lines of numpy with
 explicit bf16 rounding predict the kernels' outputs exactly:
   fused forward   out_b = rne(rne(W_b y + b_b) x)
   fused dX        dX = rne(((0 + q_0 G_0) + q_1 G_1) + q_2 G_2 + G_x),  q_b = rne(W_b y + b_b)
+  fused dY        dY = rne(sum_b W_b rne(G_b x))   (dK rounded as the MFMA operand)
 The same model without the tap rounding must differ somewhere, so the test tells the
 two readings apart.
 """
@@ -120,3 +121,43 @@ def test_weight_gradient_rounds_dk_bias_gradient_does_not(seed):
         assert pw[0, k, 0].item() == want_w, f"dW row {k}: {pw[0, k, 0].item()!r} != {want_w!r}"
         assert pb[0, k].item() == want_b, f"db row {k}: {pb[0, k].item()!r} != {want_b!r}"
         assert want_w != other_w and want_b != other_b, "case does not separate the readings"
+
+
+@pytest.mark.parametrize("seed", [41, 42])
+def test_fused_dy_rounds_dk(seed):
+    """dY = W^T rne(dK): with K = 1 and one channel, dY = rne(sum_b W_b rne(G_b x)).
+    W = (1, -1, 0) and G_1 one bfloat16 step above G_0 make the two branch terms
+    nearly cancel: the exact dK difference G_0 x - G_1 x is then far below one
+    bfloat16 step of dK, so rounding dK first or not gives different outputs.
+    Every sum is exact in float32 (differences of nearly equal values whose
+    mantissas hold at most 16 bits), so the order of the MFMA sums does not matter."""
+    H, W = 9, 70
+    x = _draw((1, 1, H, W), seed)
+    g0 = _draw((1, 1, H, W), seed + 1)
+    g0_bits = g0.view(torch.int16)
+    g1 = (g0_bits + 1).view(torch.bfloat16)  # next bfloat16 value away from zero
+    g2 = _draw((1, 1, H, W), seed + 2)
+    gx_blk = _draw((1, 1, H, W), seed + 3)
+    gout = torch.cat([gx_blk, g0, g1, g2], dim=1).contiguous()
+    w = torch.tensor([[1.0], [-1.0], [0.0]]).to(torch.bfloat16)
+    y = _draw((1, 1, H, W), seed + 4)
+    b = _draw((3,), seed + 5, 0.3)
+    gy = torch.empty_like(x, device="cuda")
+    ddpm.ddpm_fused_bwd(x.cuda(), y.cuda(), w.cuda(), b.cuda(), gout.cuda(), None, gy, None, None, 1)
+    torch.cuda.synchronize()
+    got = gy.cpu().view(torch.int16).numpy().view(np.uint16)[0, 0]
+    xv = x.float().numpy()[0, 0]
+    gv = gout.float().numpy()[0]
+    wv = w.float().numpy()[:, 0]
+
+    def model(round_dk):
+        acc = np.zeros_like(xv, dtype=np.float64)
+        for k in range(3):
+            dk = (gv[1 + k] * xv).astype(np.float32)  # exact product of two bf16 values
+            q = _rne(dk) if round_dk else dk
+            acc += np.float64(wv[k]) * q.astype(np.float64)
+        assert np.array_equal(acc.astype(np.float32).astype(np.float64), acc), "sum not exact in float32"
+        return _rne_bits(acc.astype(np.float32))
+
+    assert np.array_equal(got, model(True)), "dY is not W^T rne(dK)"
+    assert not np.array_equal(model(True), model(False)), "case does not separate the readings"

@@ -259,15 +259,19 @@ def test_bitwise_deterministic(name):
         assert torch.equal(u, v)
 
 
-def test_finite_difference_spot_check():
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_finite_difference_spot_check(dt):
     """<grad, v> from the GPU backward equals the central difference of
     L = <G, out> evaluated from GPU forwards; exact in exact arithmetic because L
-    is affine in each of x, y, weight, bias taken alone."""
+    is affine in each of x, y, weight, bias taken alone.  In bfloat16 the perturbed
+    tensors are rounded to bfloat16, so the direction is their exact difference,
+    and the tap and output rounding add noise of about 2^-9 per term."""
     shape, block = synth.WORKLOADS["nonaligned"]
-    h = inputs(shape, block, torch.float32, grad=True)
+    dtype = DT[dt]
+    h = inputs(shape, block, dtype, grad=True)
     d = dev(h)
     K = shape.K
-    announce("fd", shape)
+    announce("fd", shape, dt)
     gx, gy, gw, gb, _, _ = gpu_bwd(d, K)
     grads = {"x": gx, "y": gy, "weight": gw, "bias": gb}
     G = f64(d["grad_out"])
@@ -275,18 +279,21 @@ def test_finite_difference_spot_check():
     for name in ("x", "y", "weight", "bias"):
         v = torch.randn(d[name].shape, generator=gen).to("cuda")
         eps = 0.25
-        dp = dict(d, **{name: (d[name] + eps * v).contiguous()})
-        dm = dict(d, **{name: (d[name] - eps * v).contiguous()})
-        Lp = float((f64(gpu_fused(dp, K)) * G).sum())
-        Lm = float((f64(gpu_fused(dm, K)) * G).sum())
-        fd = (Lp - Lm) / (2 * eps)
+        base = d[name].double()
+        tp = (base + eps * v).to(dtype).contiguous()
+        tm = (base - eps * v).to(dtype).contiguous()
+        Lp = float((f64(gpu_fused(dict(d, **{name: tp}), K)) * G).sum())
+        Lm = float((f64(gpu_fused(dict(d, **{name: tm}), K)) * G).sum())
+        delta = f64(tp) - f64(tm)  # = 2 eps v in float32
+        fd = Lp - Lm
         gv = f64(grads[name])
-        vv = f64(v)
-        an = float((gv * vv).sum())
-        # Cauchy-Schwarz scale of <grad, v>; float32 rounding in the forward keeps
-        # |fd - an| far below 2e-5 of it, while a wrong or missing term does not.
-        scale = float(np.linalg.norm(gv) * np.linalg.norm(vv))
-        assert abs(fd - an) <= 2e-5 * scale + 5e-3, f"FD {name}: {fd} vs {an} (scale {scale:.3g})"
+        an = float((gv * delta).sum())
+        # Cauchy-Schwarz scale of <grad, delta>.  A wrong or missing gradient term
+        # moves <grad, delta> by about scale / sqrt(elements) (1e-2 of it here);
+        # rounding keeps |fd - an| below 2e-5 of it in float32 and 1e-3 in bfloat16.
+        scale = float(np.linalg.norm(gv) * np.linalg.norm(delta))
+        tol = 2e-5 if dt == "f32" else 1e-3
+        assert abs(fd - an) <= tol * scale + 1e-2, f"FD {name}: {fd} vs {an} (scale {scale:.3g})"
 
 
 # Special values in x: the x block of both forward outputs is a copy of x, so every
