@@ -132,15 +132,29 @@ def run_memory(args):
                 print(line, flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description="fused vs materialised DDPM: step time and peak temporary memory")
     ap.add_argument("--mode", choices=["speed", "memory", "all"], default="all")
-    ap.add_argument("--dtypes", default="f32,bf16")
-    ap.add_argument("--ks", default="3,5")
-    ap.add_argument("--memory-child", default=None, help=argparse.SUPPRESS)
-    args = ap.parse_args()
+    ap.add_argument("--dtypes", default="f32,bf16", help="comma-separated subset of f32,bf16")
+    ap.add_argument("--ks", default="3,5", help="comma-separated kernel sizes for --mode speed")
+    ap.add_argument("--memory-child", default=None, metavar="DT,PATH,H,K",
+                    help="measure one training step's temporary memory in this process and print one JSON line "
+                         "(DT f32|bf16, PATH fused|materialised)")
+    args = ap.parse_args(argv)
     args.dtypes = args.dtypes.split(",")
     args.ks = [int(k) for k in args.ks.split(",")]
+    for dt in args.dtypes:
+        if dt not in DT:
+            ap.error(f"unknown dtype {dt!r} (f32, bf16)")
+    if args.memory_child:
+        parts = args.memory_child.split(",")
+        if len(parts) != 4 or parts[0] not in DT or parts[1] not in ("fused", "materialised"):
+            ap.error("--memory-child takes DT,PATH,H,K, e.g. f32,fused,128,3")
+    return args
+
+
+def main(argv=None):
+    args = parse_args(argv)
     assert torch.cuda.is_available(), "bench_module needs a GPU"
     if args.memory_child:
         dt, path, H, K = args.memory_child.split(",")

@@ -5,6 +5,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 from dynamic_dilated_depthwise_amd import synth
 
@@ -44,3 +46,21 @@ def test_every_kernel_has_a_bound_and_sources():
     for srcs in bench.KERNEL_SOURCES.values():
         for f in srcs:
             assert os.path.exists(os.path.join(ROOT, "dynamic_dilated_depthwise_amd", "csrc", f)), f
+
+
+def test_bench_module_cli():
+    """The module benchmark's command line (no GPU: parsing only)."""
+    import subprocess
+    import sys as _sys
+    from dynamic_dilated_depthwise_amd import bench_module as bm
+    a = bm.parse_args(["--mode", "memory", "--dtypes", "bf16"])
+    assert a.mode == "memory" and a.dtypes == ["bf16"] and a.ks == [3, 5]
+    a = bm.parse_args(["--memory-child", "f32,fused,128,3"])
+    assert a.memory_child == "f32,fused,128,3"
+    for bad in (["--mode", "none"], ["--dtypes", "f16"], ["--memory-child", "f32,unfold,128,3"],
+                ["--memory-child", "f32,fused"]):
+        with pytest.raises(SystemExit):
+            bm.parse_args(bad)
+    r = subprocess.run([_sys.executable, "-m", "dynamic_dilated_depthwise_amd.bench_module", "--help"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0 and "--memory-child" in r.stdout
