@@ -26,14 +26,20 @@ and the token count N*H*W reaches the threshold for (mode, dtype, K) in
 from timing both paths on MI355X (``bench_module.py``, B=1, C=64, 16^2 .. 256^2):
 training is fused at every size except fp32 with K = 5, which is fused from
 96^2 = 9216 tokens, and inference is fused at every size.  The fused path also needs about a tenth of the
-temporary memory (the tap tensor and its gradient are never stored).  There is no
-CPU path: CPU tensors raise.
+temporary memory (the tap tensor and its gradient are never stored).
+
+CPU tensors take the CPU path of ``cpu_stream`` (section "CPU 与超大输入": one
+generator GEMM while the taps fit ``max_generated_bytes``, token tiles of
+``spatial_tile_size`` beyond it, with per-tile recompute in training when
+``recompute`` is set); device tensors never do.  Under autocast in float16 the
+materialised path filters in float32 (the library takes float32 and bfloat16).
 """
 import torch
 import torch.nn as nn
 
 from . import (ddpm_filter_bwd, ddpm_filter_fwd, ddpm_fused_bwd, ddpm_fused_fwd, ddpm_reduce_partials,
                num_partials_for)
+from .cpu_stream import DEFAULT_MAX_GENERATED_BYTES, DEFAULT_TILE_TOKENS, ddpm_cpu
 
 __all__ = ["DDPMFused", "DDPMFilter", "ddpm_fused", "ddpm_filter", "choose_path", "auto_min_tokens", "DDPM",
            "AUTO_MIN_TOKENS"]
@@ -62,7 +68,8 @@ def _autocast():
 def _check_gpu(*ts):
     for t in ts:
         if not t.is_cuda:
-            raise RuntimeError("DDPM runs on the GPU through the HIP library; CPU tensors are not supported")
+            raise RuntimeError("the HIP library takes device tensors; CPU tensors go through "
+                               "DDPM's CPU path (cpu_stream.ddpm_cpu)")
         if t.dtype not in _SUPPORTED:
             raise TypeError(f"DDPM supports float32 and bfloat16 tensors, got {t.dtype}")
 
@@ -173,16 +180,25 @@ class DDPM(nn.Module):
     for dilation b (1, 3, 5), channel c, tap t = ki*K + kj;
     filter:    [x, d1, d3, d5], zero padding D*(K-1)/2 per dilation D;
     fuse:      3x3 conv 4*dim -> dim, padding 1 (with bias).
-    x and y are [N, dim, H, W] on the GPU, float32 or bfloat16.
+    x and y are [N, dim, H, W], float32 or bfloat16, on the GPU (the HIP library)
+    or on the CPU (the CPU path).
+    spatial_tile_size / max_generated_bytes / recompute: the CPU path's token tile,
+    the tap budget beyond which it streams tiles, and per-tile recompute in
+    training (page section "使用").
     fused_generator_inference / fused_generator_training: True (fused), False
-    (materialised) or None (automatic, see the module docstring)."""
+    (materialised) or None (automatic, see the module docstring); GPU only."""
 
-    def __init__(self, dim=64, kernel_size=3, fused_generator_inference=None, fused_generator_training=None):
+    def __init__(self, dim=64, kernel_size=3, spatial_tile_size=DEFAULT_TILE_TOKENS,
+                 max_generated_bytes=DEFAULT_MAX_GENERATED_BYTES, recompute=True, fused_generator_inference=None,
+                 fused_generator_training=None):
         super().__init__()
         if kernel_size not in (1, 3, 5):
             raise ValueError("kernel_size must be 1, 3 or 5 (dilations 1, 3, 5 are fixed)")
         self.dim = dim
         self.kernel_size = kernel_size
+        self.spatial_tile_size = spatial_tile_size
+        self.max_generated_bytes = max_generated_bytes
+        self.recompute = recompute
         self.fused_generator_inference = fused_generator_inference
         self.fused_generator_training = fused_generator_training
         self.generator = nn.Conv2d(dim, 3 * dim * kernel_size * kernel_size, 1)
@@ -198,9 +214,14 @@ class DDPM(nn.Module):
 
     def dynamic_filter(self, x, y):
         """[x, d1, d3, d5] (before the fuse conv)."""
-        _check_gpu(x, y)
         K = self.kernel_size
         R = 3 * self.dim * K * K
+        if not x.is_cuda and not y.is_cuda and not self.generator.weight.is_cuda:
+            w = self.generator.weight.view(R, self.dim)
+            out, self.last_path = ddpm_cpu(x, y.to(w.dtype), w, self.generator.bias, K, self.spatial_tile_size,
+                                           self.max_generated_bytes, self.recompute)
+            return out
+        _check_gpu(x, y)
         path = self.path_for(x, y)
         self.last_path = path
         if path == "fused":
@@ -212,6 +233,10 @@ class DDPM(nn.Module):
             taps = self.generator(y)
         else:
             taps = self.generator(y.to(self.generator.weight.dtype))
+        if taps.dtype not in _SUPPORTED:
+            # float16 autocast: the library filters float32 and bfloat16; float16
+            # widens to float32 exactly
+            taps = taps.float()
         return ddpm_filter(x.to(taps.dtype), taps, K)
 
     def forward(self, x, y):

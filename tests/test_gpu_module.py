@@ -132,3 +132,26 @@ def test_autocast_bf16():
     ref, _ = _reference(m, x, y, None, shape.K)
     assert_close(f64(out), ref, TOL[torch.bfloat16]["out"], "autocast out")
     assert x.grad is not None and y.grad is not None and m.generator.weight.grad is not None
+
+
+def test_autocast_fp16():
+    """Under torch's default CUDA autocast (float16) the generator makes float16
+    taps; the library takes float32 and bfloat16, so the materialised path widens
+    the taps and x to float32 (exactly) and filters in float32.  Forward and the
+    backward into every input run, within the bfloat16 bound of fp64 (float16
+    taps carry 2^-11 relative rounding)."""
+    shape, seed = S_(1, 16, 10, 12, 3), 407
+    m = _module(shape, torch.float32, seed)
+    h = synth.make_inputs(shape, seed, torch.float32)
+    x = h["x"].cuda().requires_grad_(True)
+    y = h["y"].cuda().requires_grad_(True)
+    announce("module autocast fp16", shape)
+    with torch.autocast("cuda"):
+        out = m(x, y)
+        feats = m.dynamic_filter(x, y)
+    assert m.last_path == "materialised" and feats.dtype == torch.float32
+    out.float().sum().backward()
+    ref, _ = _reference(m, x, y, None, shape.K)
+    assert_close(f64(out), ref, TOL[torch.bfloat16]["out"], "autocast fp16 out")
+    assert x.grad is not None and y.grad is not None and m.generator.weight.grad is not None
+    assert torch.isfinite(x.grad).all() and torch.isfinite(m.generator.weight.grad).all()

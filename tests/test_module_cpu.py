@@ -1,4 +1,4 @@
-"""Host logic of the DDPM module: path choice and refusal of CPU tensors (no GPU)."""
+"""Host logic of the DDPM module: path choice, and CPU tensors taking the CPU path (no GPU)."""
 import pytest
 import torch
 
@@ -57,5 +57,10 @@ def test_module_shapes_and_refusals():
     with pytest.raises(ValueError):
         DDPM(dim=8, kernel_size=4)
     x = torch.randn(1, 8, 6, 6)
-    with pytest.raises(RuntimeError, match="CPU tensors"):
-        m(x, x)
+    out = m(x, x)                       # CPU tensors: the module's CPU path
+    assert tuple(out.shape) == (1, 8, 6, 6) and m.last_path == "cpu_direct"
+    # the library's autograd functions take device tensors only
+    from dynamic_dilated_depthwise_amd.module import ddpm_fused
+    w = m.generator.weight.view(3 * 8 * 9, 8)
+    with pytest.raises(RuntimeError, match="CPU path"):
+        ddpm_fused(x, x, w, m.generator.bias, 3)
