@@ -1,0 +1,294 @@
+// bwd_dx_bf16.hip -- dX of the fused training backward in bfloat16 for C = 64
+// (gfx950): tap recompute + gather, staged by source row.
+//
+// Operation (page "lartpang/DynamicConvolutionOperator", section
+// "CUDA Flash 式融合训练": the backward recomputes the dynamic taps and gathers
+// each dilation's contribution):
+//     dX[c, q] = G_x[c, q] + sum_{b,t} rne(T[o(b,c,t), q - d_bt]) * G_b[c, q - d_bt],
+//     T[o, p]  = bias[o] + sum_c' W[o, c'] y[c', p]      (float32 sum, one rounding).
+//
+// Work decomposition: workgroup = one 64-pixel row segment (row h, columns w0..)
+// x the 64 output channels, four waves, wave v owning channels 16v..16v+15.
+// The generator block of tap (b, t) is an MFMA product with
+//   rows    = 16 pixels (four blocks cover the segment),
+//   columns = the wave's 16 output channels,
+//   k       = the 64 input channels c' (two k-steps of 32),
+// A = y at the source pixels q - d_bt, B = weight rows (16 contiguous bytes per
+// lane).  Lane (g, i) receives the taps of channel 16v + i at four consecutive
+// pixels 16pb + 4g .. +3 of each block pb, so G_b at the same source pixels is one
+// 8-byte run per block and the products stay lane-local.
+//
+// Taps that read the same source row h - dr share one staging of y: the row's
+// segment with a column halo, all 64 channels, in LDS as eight planes of 8
+// channels ([c/8][pixel][c%8], 16 bytes per pixel), so any column shift is an
+// immediate offset and the 16 lanes of a fragment read 256 contiguous bytes.
+// Stages (7 at K = 3, 13 at K = 5, 1 at K = 1) are double-buffered with one barrier
+// each; a stage whose source row lies outside the image contributes nothing and is
+// skipped.  Every tap is unrolled at compile time, so no index arithmetic runs per
+// tap.  The sum over taps runs in stage order (float32), then G_x is added.
+#include "common.hpp"
+#include "launchers.hpp"
+
+namespace ddpm {
+namespace {
+
+constexpr int kSegX = 64;  // pixels per workgroup (one row segment)
+constexpr int kChX = 64;   // channels (input and output) this kernel serves
+
+// Stages are the (branch b, kernel row ki) pairs: the K taps of a stage read one
+// source row, h - dr with dr = (ki - r) * D_b, and one G block, G_b.
+template <int K> struct DxPlan {
+    static constexpr int r = (K - 1) / 2;
+    static constexpr int KK = K * K;
+    static constexpr int NT = 3 * KK;
+    static constexpr int NST = 3 * K;                  // stages
+    static constexpr int HALO = 5 * r;                 // largest column shift
+    static constexpr int LP = (HALO + 3) & ~3;         // staged columns left of the segment
+    static constexpr int SW = kSegX + 2 * LP;          // staged columns
+    static constexpr int PLANE = SW * 16;              // bytes of one 8-channel plane of y
+    static constexpr int YBUF = 8 * PLANE;             // bytes of one staged y row (64 channels)
+    static constexpr int GROW = SW + 4;                // elements per staged G channel row
+    static constexpr int GBUF = kChX * GROW * 2;       // bytes of one staged G row
+};
+
+// LDS image of one stage: y as eight planes of 8 channels ([c/8][pixel][c%8]) and
+// G_b as channel rows ([c][pixel], padded by 4 columns against bank conflicts).
+template <int K> struct DxStageBuf {
+    unsigned char y[DxPlan<K>::YBUF];
+    unsigned char g[DxPlan<K>::GBUF];
+};
+
+typedef uint16_t u16x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Widen a run of four bf16 values (two dwords) to float.
+__device__ __forceinline__ void widen4(const u16x4 u, float (&f)[4]) {
+    const u32x2_t d = __builtin_bit_cast(u32x2_t, u);
+    f[0] = __uint_as_float(d[0] << 16);
+    f[1] = __uint_as_float(d[0] & 0xffff0000u);
+    f[2] = __uint_as_float(d[1] << 16);
+    f[3] = __uint_as_float(d[1] & 0xffff0000u);
+}
+
+template <int K>
+__global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__restrict__ y,
+                                                             const bf16_t *__restrict__ wg,
+                                                             const bf16_t *__restrict__ bg,
+                                                             const bf16_t *__restrict__ gout,
+                                                             bf16_t *__restrict__ gx, int H, int W) {
+    using P = DxPlan<K>;
+    constexpr int r = P::r;
+    constexpr int KK = P::KK;
+    constexpr int NT = P::NT;
+    constexpr int NST = P::NST;
+    constexpr int C = kChX;
+    __shared__ __align__(16) DxStageBuf<K> sb[2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int i = lane & 15;
+    const int nseg = (W + kSegX - 1) / kSegX;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int w0 = (L % nseg) * kSegX;
+    L /= nseg;
+    const int h = L % H;
+    const int n = L / H;
+    const int HW = H * W;
+    const bf16_t *__restrict__ yn = y + (int64_t)n * C * HW;
+    const bf16_t *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
+    const int c = 16 * wave + i;  // the output channel of this lane's MFMA column
+
+    // ---- staging.  y: thread tid covers blocks of 4 channels x 4 pixels (transposed
+    // into the planes); G_b: runs of 4 pixels of one channel row (copied as they are).
+    constexpr int NB4 = P::SW / 4;            // 4-pixel runs per staged row
+    constexpr int NBLK = 16 * NB4;            // y blocks
+    constexpr int YIT = (NBLK + 255) / 256;   // y blocks per thread
+    constexpr int NRUN = kChX * NB4;          // G runs
+    constexpr int GIT = (NRUN + 255) / 256;   // G runs per thread
+    u16x4 yreg[YIT][4];
+    u16x4 greg[GIT];
+    int yoff[YIT], ydst[YIT], goff[GIT], gdst[GIT];
+    bool yok[YIT], yex[YIT], gok[GIT], gex[GIT];
+#pragma unroll
+    for (int k = 0; k < YIT; ++k) {
+        const int q = tid + 256 * k;
+        const int c4 = q / NB4;
+        const int px4 = q - c4 * NB4;
+        const int col = w0 - P::LP + 4 * px4;
+        yex[k] = q < NBLK;
+        yok[k] = yex[k] && col >= 0 && col < W;  // W % 4 == 0: a run is wholly in or out
+        yoff[k] = 4 * c4 * HW + col;
+        ydst[k] = (c4 >> 1) * P::PLANE + 4 * px4 * 16 + (c4 & 1) * 8;
+    }
+#pragma unroll
+    for (int k = 0; k < GIT; ++k) {
+        const int q = tid + 256 * k;
+        const int ch = q / NB4;
+        const int px4 = q - ch * NB4;
+        const int col = w0 - P::LP + 4 * px4;
+        gex[k] = q < NRUN;
+        gok[k] = gex[k] && col >= 0 && col < W;
+        goff[k] = ch * HW + col;
+        gdst[k] = (ch * P::GROW + 4 * px4) * 2;
+    }
+    // global loads of stage st (branch b = st / K, kernel row ki = st % K) into registers
+    auto load_stage = [&](int st) {
+        const int b = st / K;
+        const int ki = st - b * K;
+        const int hs = h - (ki - r) * (1 + 2 * b);
+        if (hs < 0 || hs >= H) return;  // wave-uniform: the stage is skipped
+        const bf16_t *ybase = yn + hs * W;
+        const bf16_t *gbase = gn + (1 + b) * C * HW + hs * W;
+#pragma unroll
+        for (int k = 0; k < YIT; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u16x4 v = {0, 0, 0, 0};
+                if (yok[k]) v = *(const u16x4 *)(ybase + yoff[k] + e * HW);
+                yreg[k][e] = v;
+            }
+#pragma unroll
+        for (int k = 0; k < GIT; ++k) {
+            u16x4 v = {0, 0, 0, 0};
+            if (gok[k]) v = *(const u16x4 *)(gbase + goff[k]);
+            greg[k] = v;
+        }
+    };
+    auto store_stage = [&](int st, int buf) {
+        const int b = st / K;
+        const int ki = st - b * K;
+        const int hs = h - (ki - r) * (1 + 2 * b);
+        if (hs < 0 || hs >= H) return;
+#pragma unroll
+        for (int k = 0; k < YIT; ++k) {
+            if (!yex[k]) continue;
+            unsigned char *d = sb[buf].y + ydst[k];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                u16x4 o;
+                o[0] = yreg[k][0][p]; o[1] = yreg[k][1][p]; o[2] = yreg[k][2][p]; o[3] = yreg[k][3][p];
+                *(u16x4 *)(d + 16 * p) = o;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < GIT; ++k)
+            if (gex[k]) *(u16x4 *)(sb[buf].g + gdst[k]) = greg[k];
+    };
+
+    // ---- the tap loop.  Weight fragments of tap (b, t): row o = (b*C + c)*KK + t,
+    // columns 32 sub + 8g .. +7, and the row's bias; fetched two taps ahead (a ring
+    // of three).
+    const bf16_t *__restrict__ wl = wg + c * KK * C + 8 * g;
+    const bf16_t *__restrict__ bgl = bg + c * KK;
+    struct WOps { bf16x8 b0, b1; bf16_t bias; };
+    WOps wring[3];
+    auto fetch_w = [&](int bt, WOps &o) {  // bt = b*KK + t
+        const int b = bt / KK;
+        const int t = bt - b * KK;
+        const bf16_t *wt = wl + (b * C * KK + t) * C;
+        o.b0 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(wt));
+        o.b1 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(wt + 32));
+        o.bias = bgl[b * C * KK + t];
+    };
+    // A fragment (y): plane 4*sub + g, pixel 16pb + i + (LP - dc)
+    const int a_lane = g * P::PLANE + i * 16;
+    // G_b run: channel c, pixels 16pb + 4g + (LP - dc) .. +3 of the staged row
+    const int g_lane = (c * P::GROW + 4 * g) * 2;
+
+    float dacc[4][4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dacc[pb][v] = 0.f;
+
+    load_stage(0);
+    store_stage(0, 0);
+    fetch_w(0, wring[0]);
+    if (NT > 1) fetch_w(1, wring[1]);
+    if (NST > 1) load_stage(1);
+    __syncthreads();
+
+#pragma clang loop unroll(full)
+    for (int st = 0; st < NST; ++st) {
+        const int b = st / K;
+        const int ki = st - b * K;
+        const int D = 1 + 2 * b;
+        const int hs = h - (ki - r) * D;
+        const bool rok = hs >= 0 && hs < H;  // wave-uniform: taps reading outside the image add nothing
+        const unsigned char *ybuf = sb[st & 1].y;
+        const unsigned char *gbuf = sb[st & 1].g;
+#pragma clang loop unroll(full)
+        for (int kj = 0; kj < K; ++kj) {
+            const int bt = b * KK + ki * K + kj;  // this tap; taps run in (b, t) order
+            const WOps cur = wring[bt % 3];
+            if (bt + 2 < NT) fetch_w(bt + 2, wring[(bt + 2) % 3]);
+            if (rok) {
+                const int dc = (kj - r) * D;
+                const float bias = bf16_bits_to_f32(cur.bias);
+                const f32x4 bias4 = {bias, bias, bias, bias};
+                const unsigned char *ab = ybuf + a_lane + (P::LP - dc) * 16;
+                const unsigned char *gb = gbuf + g_lane + (P::LP - dc) * 2;
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const bf16x8 a0 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(ab + pb * 256));
+                    const bf16x8 a1 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(ab + pb * 256 + 4 * P::PLANE));
+                    const u16x4 graw = *(const u16x4_a2 *)(gb + pb * 32);
+                    f32x4 acc = mfma_16x16x32_bf16(a0, cur.b0, bias4);
+                    acc = mfma_16x16x32_bf16(a1, cur.b1, acc);
+                    float gf[4];
+                    widen4(graw, gf);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) dacc[pb][v] += round_to_bf16(acc[v]) * gf[v];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (st + 1 < NST) {
+            store_stage(st + 1, (st + 1) & 1);
+            __syncthreads();
+            if (st + 2 < NST) load_stage(st + 2);
+        }
+    }
+
+    // dX = G_x + the gathered sum, rounded once
+    const bf16_t *gxr = gn + c * HW + h * W + w0 + 4 * g;
+    bf16_t *dst = gx + (int64_t)n * C * HW + c * HW + h * W + w0 + 4 * g;
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+        if (w0 + 16 * pb + 4 * g >= W) continue;  // W % 4 == 0: runs are whole
+        float gf[4];
+        widen4(*(const u16x4 *)(gxr + 16 * pb), gf);
+        u16x4 o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_bits(dacc[pb][v] + gf[v]);
+        *(u16x4 *)(dst + 16 * pb) = o;
+    }
+}
+
+}  // namespace
+
+// Applicability: bfloat16, C = 64, W % 4 == 0, 16-byte aligned tensors (checked by
+// the caller) and plane offsets within 32 bits.
+bool bwd_dx_bf16_applies(int C, int H, int W, bool al) {
+    return C == kChX && al && (W % 4) == 0 && (int64_t)4 * kChX * H * W < (int64_t(1) << 31);
+}
+
+hipError_t launch_bwd_dx_bf16(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
+                              int H, int W, int K, hipStream_t stream) {
+    const int64_t nblk = (int64_t)N * H * ((W + kSegX - 1) / kSegX);
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)nblk), block(256);
+    const bf16_t *Y = (const bf16_t *)y, *Wg = (const bf16_t *)wg, *Bg = (const bf16_t *)bg,
+                 *G = (const bf16_t *)gout;
+    bf16_t *GX = (bf16_t *)gx;
+    switch (K) {
+        case 1: hipLaunchKernelGGL(bwd_dx_bf16_kernel<1>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
+        case 3: hipLaunchKernelGGL(bwd_dx_bf16_kernel<3>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
+        default: hipLaunchKernelGGL(bwd_dx_bf16_kernel<5>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ddpm

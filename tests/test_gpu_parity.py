@@ -58,6 +58,11 @@ BWD_CASES = [
     # two 64-channel blocks at K = 1, and a grid of two workgroups per CU (eight-wave
     # dY, two wave groups in dX) on the workload's channel count
     ("c128_k1_w64", (S_(1, 128, 12, 64, 1), 218)), ("c64_mid_grid", (S_(1, 64, 96, 192, 3), 219)),
+    # C = 64 grids of more than two row segments per CU (the row-staged bf16 dX):
+    # a partial last segment (100 = 64 + 36 columns) in a batch of two, K = 1 with one
+    # segment per row, and K = 5 with a ragged 200-column row and 130 rows
+    ("c64_w100_batch2", (S_(2, 64, 160, 100, 3), 220)), ("c64_k1_tall", (S_(1, 64, 520, 64, 1), 221)),
+    ("c64_k5_w200", (S_(1, 64, 130, 200, 5), 222)),
 ]
 
 
