@@ -470,8 +470,8 @@ hipError_t launch_dx_t(const void *y, const void *wg, const void *bg, const void
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), 0, stream, (const T *)y, (const T *)wg,
                            (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
     };
-    if (Elem<T>::is_bf16 && nblk > 2 * kCUs && bwd_dx_bf16_applies(C, H, W, al))
-        return launch_bwd_dx_bf16(y, wg, bg, gout, gx, N, H, W, K, stream);
+    if (nblk > 2 * kCUs && bwd_dx_rows_applies(C, H, W, al))
+        return launch_bwd_dx_rows(y, wg, bg, gout, gx, N, H, W, K, Elem<T>::is_bf16, stream);
     if (nblk <= kCUs) {
         if (fullw) launch(bwd_dx_kernel<T, K, 4, !Elem<T>::is_bf16>, 1024);
         else launch(bwd_dx_kernel<T, K, 4, false>, 1024);

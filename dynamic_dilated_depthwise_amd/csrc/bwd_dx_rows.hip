@@ -1,5 +1,5 @@
-// bwd_dx_bf16.hip -- dX of the fused training backward in bfloat16 for C = 64
-// (gfx950): tap recompute + gather, staged by source row.
+// bwd_dx_rows.hip -- dX of the fused training backward for C = 64 (gfx950), in
+// bfloat16 and float32: tap recompute + gather, staged by source row.
 //
 // Operation (page "lartpang/DynamicConvolutionOperator", section
 // "CUDA Flash 式融合训练": the backward recomputes the dynamic taps and gathers
@@ -267,19 +267,251 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
     }
 }
 
+// ---------------------------------------------------------------------------- float32
+// The same decomposition in float32 with v_mfma_f32_16x16x4_f32: MFMA rows = 16
+// pixels (blocks pb = 0..3 cover the segment), columns = the wave's 16 output
+// channels, and k-step s (0..15) takes input channel 16g + s from lane group g, so
+// a lane's A values for one pixel block are 16 contiguous channels of one pixel
+// (four 16-byte LDS reads) and its B values 16 contiguous weights of one row (four
+// 16-byte loads).  A tap is 64 MFMAs per wave.  Per (branch, kernel row) stage, y
+// is staged as [pixel][64 channels + 4 pad] (272-byte pixel rows: the 16 pixels of
+// a fragment start in distinct 4-dword bank groups) and G_b as channel rows of 84
+// floats (the 16 channels of a read start in distinct 4-dword bank groups), each
+// once per stage and read at the K column shifts of its taps; one LDS image,
+// written between two barriers, its global loads issued a whole stage ahead.  The
+// weight rows come from global memory one tap ahead.
+template <int K> struct DxPlanF {
+    static constexpr int r = (K - 1) / 2;
+    static constexpr int KK = K * K;
+    static constexpr int NT = 3 * KK;
+    static constexpr int NST = 3 * K;
+    static constexpr int HALO = 5 * r;
+    static constexpr int LP = (HALO + 3) & ~3;
+    static constexpr int SW = kSegX + 2 * LP;
+    static constexpr int PROW = kChX + 4;         // floats per staged y pixel
+    static constexpr int YBUF = SW * PROW;        // floats of the staged y row
+    static constexpr int GROW = ((SW + 12) / 16) * 16 + 4;  // floats per staged G channel row (== 4 mod 16)
+    static constexpr int GBUF = kChX * GROW;      // floats of the staged G row
+};
+
+template <int K>
+__global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restrict__ y,
+                                                            const float *__restrict__ wg,
+                                                            const float *__restrict__ bg,
+                                                            const float *__restrict__ gout,
+                                                            float *__restrict__ gx, int H, int W) {
+    using P = DxPlanF<K>;
+    constexpr int r = P::r;
+    constexpr int KK = P::KK;
+    constexpr int NT = P::NT;
+    constexpr int NST = P::NST;
+    constexpr int C = kChX;
+    __shared__ __align__(16) float ys[P::YBUF];
+    __shared__ __align__(16) float gs[P::GBUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int i = lane & 15;
+    const int nseg = (W + kSegX - 1) / kSegX;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int w0 = (L % nseg) * kSegX;
+    L /= nseg;
+    const int h = L % H;
+    const int n = L / H;
+    const int HW = H * W;
+    const float *__restrict__ yn = y + (int64_t)n * C * HW;
+    const float *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
+    const int c = 16 * wave + i;  // the output channel of this lane's MFMA column
+
+    // ---- staging.  y: thread tid covers blocks of 4 channels x 4 pixels, transposed
+    // in registers into four pixel entries of 4 channels; G_b: runs of 4 pixels of
+    // one channel row, copied as they are.  Runs outside the image (W % 4 == 0:
+    // wholly in or out) load the row's first run and are zeroed.
+    constexpr int NB4 = P::SW / 4;
+    constexpr int NBLK = 16 * NB4;
+    constexpr int YIT = (NBLK + 255) / 256;
+    constexpr int NRUN = kChX * NB4;
+    constexpr int GIT = (NRUN + 255) / 256;
+    f32x4 yreg[YIT][4];
+    f32x4 greg[GIT];
+    unsigned yoff[YIT], goff[GIT];
+    int ydst[YIT], gdst[GIT];
+    bool yok[YIT], yex[YIT], gok[GIT], gex[GIT];
+#pragma unroll
+    for (int k = 0; k < YIT; ++k) {
+        const int q = tid + 256 * k;
+        const int c4 = q / NB4;
+        const int px4 = q - c4 * NB4;
+        const int col = w0 - P::LP + 4 * px4;
+        yex[k] = q < NBLK;
+        yok[k] = yex[k] && col >= 0 && col < W;
+        yoff[k] = (unsigned)(4 * (yex[k] ? c4 : 0) * HW + (yok[k] ? col : 0));
+        ydst[k] = 4 * px4 * P::PROW + 4 * c4;
+    }
+#pragma unroll
+    for (int k = 0; k < GIT; ++k) {
+        const int q = tid + 256 * k;
+        const int ch = q / NB4;
+        const int px4 = q - ch * NB4;
+        const int col = w0 - P::LP + 4 * px4;
+        gex[k] = q < NRUN;
+        gok[k] = gex[k] && col >= 0 && col < W;
+        goff[k] = (unsigned)((gex[k] ? ch : 0) * HW + (gok[k] ? col : 0));
+        gdst[k] = ch * P::GROW + 4 * px4;
+    }
+    auto stage_row = [&](int st) {  // the stage's source row (may lie outside the image)
+        const int b = st / K;
+        const int ki = st - b * K;
+        return h - (ki - r) * (1 + 2 * b);
+    };
+    auto load_stage = [&](int st) {
+        const int hs = stage_row(st);
+        if (hs < 0 || hs >= H) return;  // wave-uniform: the stage is skipped
+        const float *ybase = yn + hs * W;
+        const float *gbase = gn + (1 + st / K) * C * HW + hs * W;
+#pragma unroll
+        for (int k = 0; k < YIT; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x4 v = *(const f32x4 *)(ybase + (yoff[k] + (unsigned)(e * HW)));
+                yreg[k][e] = yok[k] ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int k = 0; k < GIT; ++k) {
+            const f32x4 v = *(const f32x4 *)(gbase + goff[k]);
+            greg[k] = gok[k] ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto store_stage = [&](int st) {
+        const int hs = stage_row(st);
+        if (hs < 0 || hs >= H) return;
+#pragma unroll
+        for (int k = 0; k < YIT; ++k) {
+            if (!yex[k]) continue;
+            float *d = ys + ydst[k];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                *(f32x4 *)(d + p * P::PROW) = f32x4{yreg[k][0][p], yreg[k][1][p], yreg[k][2][p], yreg[k][3][p]};
+        }
+#pragma unroll
+        for (int k = 0; k < GIT; ++k)
+            if (gex[k]) *(f32x4 *)(gs + gdst[k]) = greg[k];
+    };
+
+    // ---- weight rows from global memory, one tap ahead: tap (b, t) for channel c,
+    // columns 16g .. 16g+15, and its bias
+    const float *__restrict__ wl = wg + c * KK * C + 16 * g;
+    const float *__restrict__ bgl = bg + c * KK;
+    struct WOps {
+        f32x4 w[4];
+        float bias;
+    };
+    auto fetch = [&](int bt, WOps &o) {  // bt = b*KK + t
+        const int b = bt / KK;
+        const int t = bt - b * KK;
+        const float *wt = wl + (b * C * KK + t) * C;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o.w[q] = *(const f32x4 *)(wt + 4 * q);
+        o.bias = bgl[b * C * KK + t];
+    };
+
+    float dacc[4][4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dacc[pb][v] = 0.f;
+
+    WOps ring[2];  // operands of tap bt in ring[bt & 1]
+    load_stage(0);
+    fetch(0, ring[0]);
+    // A fragment: pixel 16pb + i + (LP - dc), channels 16g .. 16g + 15
+    const int a_lane = i * P::PROW + 16 * g;
+    // G_b run: channel c, pixels 16pb + 4g + (LP - dc) .. +3
+    const int g_lane = c * P::GROW + 4 * g;
+#pragma clang loop unroll(full)
+    for (int st = 0; st < NST; ++st) {
+        const int b = st / K;
+        const int ki = st - b * K;
+        const int D = 1 + 2 * b;
+        const int hs = h - (ki - r) * D;
+        const bool rok = hs >= 0 && hs < H;  // wave-uniform: taps reading outside the image add nothing
+        if (st > 0) __syncthreads();  // every wave is done reading the previous stage
+        store_stage(st);
+        __syncthreads();
+        if (st + 1 < NST) load_stage(st + 1);
+#pragma clang loop unroll(full)
+        for (int kj = 0; kj < K; ++kj) {
+            const int bt = b * KK + ki * K + kj;
+            const WOps &cur = ring[bt & 1];
+            if (bt + 1 < NT) fetch(bt + 1, ring[(bt + 1) & 1]);
+            if (rok) {
+                const int dc = (kj - r) * D;
+                const float *ab = ys + a_lane + (P::LP - dc) * P::PROW;
+                const float *gb = gs + g_lane + (P::LP - dc);
+                // the A reads of block pb + 1 are issued before block pb's MFMAs
+                f32x4 a[2][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a[0][q] = *(const f32x4 *)(ab + 4 * q);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    if (pb + 1 < 4) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            a[(pb + 1) & 1][q] = *(const f32x4 *)(ab + (pb + 1) * 16 * P::PROW + 4 * q);
+                    }
+                    const f32x4 gv = *(const f32x4_a4 *)(gb + 16 * pb);
+                    __builtin_amdgcn_sched_barrier(0);
+                    f32x4 acc = {cur.bias, cur.bias, cur.bias, cur.bias};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc = mfma_16x16x4_f32(a[pb & 1][q][e], cur.w[q][e], acc);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) dacc[pb][v] += acc[v] * gv[v];
+                }
+            }
+        }
+    }
+
+    // dX = G_x + the gathered sum
+    const float *gxr = gn + c * HW + h * W + w0 + 4 * g;
+    float *dst = gx + (int64_t)n * C * HW + c * HW + h * W + w0 + 4 * g;
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+        if (w0 + 16 * pb + 4 * g >= W) continue;  // W % 4 == 0: runs are whole
+        const f32x4 gxv = *(const f32x4 *)(gxr + 16 * pb);
+        f32x4 o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = dacc[pb][v] + gxv[v];
+        *(f32x4 *)(dst + 16 * pb) = o;
+    }
+}
+
 }  // namespace
 
-// Applicability: bfloat16, C = 64, W % 4 == 0, 16-byte aligned tensors (checked by
-// the caller) and plane offsets within 32 bits.
-bool bwd_dx_bf16_applies(int C, int H, int W, bool al) {
+// Applicability: C = 64, W % 4 == 0, 16-byte aligned tensors (checked by the
+// caller) and plane offsets within 32 bits.
+bool bwd_dx_rows_applies(int C, int H, int W, bool al) {
     return C == kChX && al && (W % 4) == 0 && (int64_t)4 * kChX * H * W < (int64_t(1) << 31);
 }
 
-hipError_t launch_bwd_dx_bf16(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
-                              int H, int W, int K, hipStream_t stream) {
+hipError_t launch_bwd_dx_rows(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
+                              int H, int W, int K, bool bf16, hipStream_t stream) {
     const int64_t nblk = (int64_t)N * H * ((W + kSegX - 1) / kSegX);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nblk), block(256);
+    if (!bf16) {
+        const float *Y = (const float *)y, *Wg = (const float *)wg, *Bg = (const float *)bg, *G = (const float *)gout;
+        float *GX = (float *)gx;
+        switch (K) {
+            case 1: hipLaunchKernelGGL(bwd_dx_f32_kernel<1>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
+            case 3: hipLaunchKernelGGL(bwd_dx_f32_kernel<3>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
+            default: hipLaunchKernelGGL(bwd_dx_f32_kernel<5>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
+        }
+        return hipGetLastError();
+    }
     const bf16_t *Y = (const bf16_t *)y, *Wg = (const bf16_t *)wg, *Bg = (const bf16_t *)bg,
                  *G = (const bf16_t *)gout;
     bf16_t *GX = (bf16_t *)gx;

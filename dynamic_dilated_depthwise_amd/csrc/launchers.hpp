@@ -25,11 +25,11 @@ int64_t bwd_dx_blocks(int N, int C, int H, int W);
 hipError_t launch_bwd_dx(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N, int C,
                          int H, int W, int K, bool bf16, bool al, hipStream_t stream);
 
-// dX in bfloat16 for C = 64 (row-staged kernel); bwd_dx_bf16_applies tells whether
-// a shape can take it.
-bool bwd_dx_bf16_applies(int C, int H, int W, bool al);
-hipError_t launch_bwd_dx_bf16(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
-                              int H, int W, int K, hipStream_t stream);
+// dX for C = 64 staged by source row (both dtypes); bwd_dx_rows_applies tells
+// whether a shape can take it.
+bool bwd_dx_rows_applies(int C, int H, int W, bool al);
+hipError_t launch_bwd_dx_rows(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
+                              int H, int W, int K, bool bf16, hipStream_t stream);
 
 // gx or gtaps may be null: that output is skipped (not both).
 hipError_t launch_filter_bwd(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N, int C,
