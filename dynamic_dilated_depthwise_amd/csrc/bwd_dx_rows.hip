@@ -292,6 +292,14 @@ template <int K> struct DxPlanF {
     static constexpr int YBUF = SW * PROW;        // floats of the staged y row
     static constexpr int GROW = ((SW + 12) / 16) * 16 + 4;  // floats per staged G channel row (== 4 mod 16)
     static constexpr int GBUF = kChX * GROW;      // floats of the staged G row
+    // Stage order: the 3(K-1) (branch, kernel row) pairs with a row shift first
+    // (branch-major), then the three unshifted kernel rows (ki = r) of branches
+    // 0, 1, 2, which read the same y row and stage it once.
+    static constexpr int NSHIFT = 3 * (K - 1);
+    static constexpr int KM = K > 1 ? K - 1 : 1;  // shifted kernel rows per branch (K = 1: none)
+    static constexpr int stage_b(int s) { return s < NSHIFT ? s / KM : s - NSHIFT; }
+    static constexpr int stage_ki(int s) { return s < NSHIFT ? (s % KM < r ? s % KM : s % KM + 1) : r; }
+    static constexpr bool new_y(int s) { return s <= NSHIFT; }  // stage s stages its own y row
 };
 
 template <int K>
@@ -330,8 +338,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
     // one channel row, copied as they are.  Runs outside the image (W % 4 == 0:
     // wholly in or out) load the row's first run and are zeroed.
     constexpr int NB4 = P::SW / 4;
-    constexpr int NBLK = 16 * NB4;
-    constexpr int YIT = (NBLK + 255) / 256;
+    constexpr int YIT = (NB4 + 15) / 16;   // y blocks per thread (16 runs of 4 pixels per iteration)
     constexpr int NRUN = kChX * NB4;
     constexpr int GIT = (NRUN + 255) / 256;
     f32x4 yreg[YIT][4];
@@ -339,15 +346,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
     unsigned yoff[YIT], goff[GIT];
     int ydst[YIT], gdst[GIT];
     bool yok[YIT], yex[YIT], gok[GIT], gex[GIT];
+    // y block of thread tid, iteration k: channel quad c4 = (tid / 4) % 16, 4-pixel
+    // run px4 = 4 * (tid / 64 + 4k) + tid % 4.  Four lanes read 64 contiguous bytes
+    // of one channel row, and the 16 lanes of a quarter wave write pixel entries
+    // whose 16-byte pieces fall in distinct bank groups (pixel rows are 68 floats).
 #pragma unroll
     for (int k = 0; k < YIT; ++k) {
-        const int q = tid + 256 * k;
-        const int c4 = q / NB4;
-        const int px4 = q - c4 * NB4;
+        const int c4 = (tid >> 2) & 15;
+        const int px4 = 4 * ((tid >> 6) + 4 * k) + (tid & 3);
         const int col = w0 - P::LP + 4 * px4;
-        yex[k] = q < NBLK;
+        yex[k] = px4 < NB4;
         yok[k] = yex[k] && col >= 0 && col < W;
-        yoff[k] = (unsigned)(4 * (yex[k] ? c4 : 0) * HW + (yok[k] ? col : 0));
+        yoff[k] = (unsigned)(4 * c4 * HW + (yok[k] ? col : 0));
         ydst[k] = 4 * px4 * P::PROW + 4 * c4;
     }
 #pragma unroll
@@ -362,22 +372,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
         gdst[k] = ch * P::GROW + 4 * px4;
     }
     auto stage_row = [&](int st) {  // the stage's source row (may lie outside the image)
-        const int b = st / K;
-        const int ki = st - b * K;
-        return h - (ki - r) * (1 + 2 * b);
+        return h - (P::stage_ki(st) - r) * (1 + 2 * P::stage_b(st));
     };
     auto load_stage = [&](int st) {
         const int hs = stage_row(st);
         if (hs < 0 || hs >= H) return;  // wave-uniform: the stage is skipped
         const float *ybase = yn + hs * W;
-        const float *gbase = gn + (1 + st / K) * C * HW + hs * W;
+        const float *gbase = gn + (1 + P::stage_b(st)) * C * HW + hs * W;
+        if (P::new_y(st)) {
 #pragma unroll
-        for (int k = 0; k < YIT; ++k)
+            for (int k = 0; k < YIT; ++k)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f32x4 v = *(const f32x4 *)(ybase + (yoff[k] + (unsigned)(e * HW)));
-                yreg[k][e] = yok[k] ? v : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const f32x4 v = *(const f32x4 *)(ybase + (yoff[k] + (unsigned)(e * HW)));
+                    yreg[k][e] = yok[k] ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
 #pragma unroll
         for (int k = 0; k < GIT; ++k) {
             const f32x4 v = *(const f32x4 *)(gbase + goff[k]);
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
         if (hs < 0 || hs >= H) return;
 #pragma unroll
         for (int k = 0; k < YIT; ++k) {
-            if (!yex[k]) continue;
+            if (!P::new_y(st) || !yex[k]) continue;
             float *d = ys + ydst[k];
 #pragma unroll
             for (int p = 0; p < 4; ++p)
@@ -423,17 +433,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
 #pragma unroll
         for (int v = 0; v < 4; ++v) dacc[pb][v] = 0.f;
 
-    WOps ring[2];  // operands of tap bt in ring[bt & 1]
+    WOps ring[2];  // operands of the ti-th tap of the stage order in ring[ti & 1]
     load_stage(0);
-    fetch(0, ring[0]);
+    fetch(P::stage_b(0) * KK + P::stage_ki(0) * K, ring[0]);
     // A fragment: pixel 16pb + i + (LP - dc), channels 16g .. 16g + 15
     const int a_lane = i * P::PROW + 16 * g;
     // G_b run: channel c, pixels 16pb + 4g + (LP - dc) .. +3
     const int g_lane = c * P::GROW + 4 * g;
 #pragma clang loop unroll(full)
     for (int st = 0; st < NST; ++st) {
-        const int b = st / K;
-        const int ki = st - b * K;
+        const int b = P::stage_b(st);
+        const int ki = P::stage_ki(st);
         const int D = 1 + 2 * b;
         const int hs = h - (ki - r) * D;
         const bool rok = hs >= 0 && hs < H;  // wave-uniform: taps reading outside the image add nothing
@@ -443,9 +453,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
         if (st + 1 < NST) load_stage(st + 1);
 #pragma clang loop unroll(full)
         for (int kj = 0; kj < K; ++kj) {
+            const int ti = st * K + kj;  // position in the tap order
             const int bt = b * KK + ki * K + kj;
-            const WOps &cur = ring[bt & 1];
-            if (bt + 1 < NT) fetch(bt + 1, ring[(bt + 1) & 1]);
+            const WOps &cur = ring[ti & 1];
+            if (ti + 1 < NT) {
+                const int sn = (kj + 1 < K) ? st : st + 1;
+                const int kn = (kj + 1 < K) ? kj + 1 : 0;
+                fetch(P::stage_b(sn) * KK + P::stage_ki(sn) * K + kn, ring[(ti + 1) & 1]);
+            }
             if (rok) {
                 const int dc = (kj - r) * D;
                 const float *ab = ys + a_lane + (P::LP - dc) * P::PROW;
