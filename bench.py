@@ -81,13 +81,16 @@ KERNEL_BOUND = {"filter": "hbm", "fused_fwd": "mfma", "bwd_dx": "mfma", "bwd_dy"
                 "reduce": "hbm", "filter_bwd": "hbm"}
 
 # Kernel symbol and the source files that define it (for the traffic record's digest).
-KERNEL_SYMBOL = {"filter": "filter_fwd_kernel", "fused_fwd": "fused_fwd_kernel", "bwd_dx": "bwd_dx_kernel",
+# dX at C = 64 on grids of more than two row segments per CU runs the row-staged
+# kernels of bwd_dx_rows.hip (one per dtype).
+KERNEL_SYMBOL = {"filter": "filter_fwd_kernel", "fused_fwd": "fused_fwd_kernel",
+                 "bwd_dx": {"f32": "bwd_dx_f32_kernel", "bf16": "bwd_dx_bf16_kernel"},
                  "bwd_dy": "bwd_dy_kernel", "bwd_dw": "bwd_dw_kernel", "reduce": "reduce_partials_kernel",
                  "filter_bwd": "filter_bwd_kernel"}
 KERNEL_SOURCES = {
     "filter": ["filter_fwd.hip", "common.hpp"],
     "fused_fwd": ["fused_fwd.hip", "gen_mma.hpp", "common.hpp"],
-    "bwd_dx": ["bwd_dx.hip", "gen_mma.hpp", "common.hpp"],
+    "bwd_dx": ["bwd_dx.hip", "bwd_dx_rows.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dy": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dw": ["fused_bwd.hip", "gen_mma.hpp", "common.hpp"],
     "reduce": ["reduce.hip", "common.hpp"],
@@ -114,9 +117,12 @@ def recorded_traffic(name, workload, dtype):
     path = os.path.join(PROFILES, f"traffic_{workload}_{dtype}.md")
     if not os.path.exists(path):
         return None
+    sym = KERNEL_SYMBOL[name]
+    if isinstance(sym, dict):
+        sym = sym[dtype]
     for line in open(path):
         parts = line.split()
-        if len(parts) >= 4 and parts[0] == "traffic:" and parts[1] == KERNEL_SYMBOL[name]:
+        if len(parts) >= 4 and parts[0] == "traffic:" and parts[1] == sym:
             fields = dict(p.split("=", 1) for p in parts[2:] if "=" in p)
             if fields.get("source") == kernel_source_digest(name):
                 return int(fields["bytes"])
