@@ -586,8 +586,11 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
         hipError_t e = launch_bwd_dx(y, wg, bg, gout, gx, N, C, H, W, K, Elem<T>::is_bf16, al, stream);
         if (e != hipSuccess) return e;
     }
-    // dY
-    if (gy != nullptr) {
+    // dY (float32, C = 64 and more than two row segments per CU: bwd_dy_rows.hip)
+    if (gy != nullptr && !Elem<T>::is_bf16 && nblk_dy > 2 * kCUs && bwd_dy_rows_applies(C, H, W, al)) {
+        hipError_t e = launch_bwd_dy_rows(x, wg, gout, gy, N, H, W, K, stream);
+        if (e != hipSuccess) return e;
+    } else if (gy != nullptr) {
         const dim3 grid((unsigned)nblk_dy);
         const int mb = (C >= 64) ? 4 : (C + 15) / 16;
         // eight waves per workgroup when the grid gives at most two workgroups per CU;
