@@ -22,6 +22,20 @@
 // The B operand dK is formed in registers from the staged G and x.  The four waves'
 // partial sums are added in wave order through LDS at the end; a stage whose x row
 // lies outside the image contributes nothing and is skipped.
+//
+// bfloat16 (bwd_dy_bf16_kernel): one MFMA k-step covers 32 input channels, so the
+// waves split pixels instead and each forms dK only for its own pixels, once:
+// workgroup = one 256-pixel row segment, wave v = pixels 64v .. 64v+63 x all 64
+// output channels (v_mfma_f32_16x16x32_bf16):
+//   rows    = 16 pixels 16pb + i of the wave (four blocks pb);
+//   columns = 16 output channels 16nb + j (four blocks nb);
+//   k       = 32 input channels 32ks + 8g + e (two k-steps ks).
+// x and G_b are staged as [channel/8][pixel][8] so that a lane's eight channels of
+// one pixel are one 16-byte LDS read at any column shift; each wave keeps its
+// pixels' G_b in float32 registers for a whole branch.  The K taps' weight rows of
+// a stage are staged as they are stored ([c][c'] per tap) and read transposed into
+// the B layout with ds_read_b64_tr_b16.  dK = rne(G * x) (exact product, one
+// rounding) is the A operand; the sums stay in float32 and are rounded once.
 #include "common.hpp"
 #include "launchers.hpp"
 
@@ -239,19 +253,276 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
     }
 }
 
+
+// ============================================================================ bfloat16
+constexpr int kSegB = 256;  // pixels per workgroup (four waves x 64)
+
+template <int K> struct DyPlanB {
+    static constexpr int r = (K - 1) / 2;
+    static constexpr int KK = K * K;
+    static constexpr int NST = 3 * K;            // (branch, kernel row) stages, branch-major
+    static constexpr int HALO = 5 * r;
+    static constexpr int LP = (HALO + 7) & ~7;   // staged x pixels left of the segment (8-pixel runs)
+    static constexpr int XS = kSegB + 2 * LP;    // staged x pixels
+    // 16-byte slots per channel-group plane: one more than a multiple of 16, so the
+    // staging writes of 16 consecutive lanes (8 planes x 2 runs) hit distinct banks
+    static constexpr int XP = (XS + 15) / 16 * 16 + 1;
+    static constexpr int GP = kSegB + 1;
+    static constexpr int WR = 80;                // bf16 elements per staged weight row (64 + pad)
+    static constexpr int NXI = XS;               // x items (8 channels x 8 pixels): 8 planes x XS/8
+    static constexpr int XIT = (NXI + 255) / 256;
+    static constexpr int WIT = 2 * K;            // 16-byte weight slots per thread per stage
+    static constexpr int XOFF = 0;               // byte offsets of the LDS regions
+    static constexpr int GOFF = XOFF + 8 * XP * 16;
+    static constexpr int WOFF = GOFF + 8 * GP * 16;
+    static constexpr int LDS = WOFF + K * 64 * WR * 2;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Eight channel runs of eight pixels (u[e] = channel e, pixels 0..7 as bf16 pairs)
+// to eight pixel runs of eight channels (o[k] = pixel k, channels 0..7): each output
+// pair is one v_perm_b32, whose selector bytes 0-3 address the second operand's
+// bytes and 4-7 the first's (low halves: 0x05040100, high halves: 0x07060302).
+__device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&u)[8], u32x4 (&o)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            o[k][m] = __builtin_amdgcn_perm(u[2 * m + 1][k >> 1], u[2 * m][k >> 1],
+                                            (k & 1) ? 0x07060302u : 0x05040100u);
+}
+
+template <int K>
+__global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__restrict__ x,
+                                                             const bf16_t *__restrict__ wg,
+                                                             const bf16_t *__restrict__ gout,
+                                                             bf16_t *__restrict__ gy, int H, int W) {
+    using P = DyPlanB<K>;
+    constexpr int r = P::r;
+    constexpr int KK = P::KK;
+    constexpr int NST = P::NST;
+    constexpr int C = kChY;
+    extern __shared__ __align__(16) unsigned char lds_b[];
+    bf16_t *xs = (bf16_t *)(lds_b + P::XOFF);  // [8][XP][8]
+    bf16_t *gs = (bf16_t *)(lds_b + P::GOFF);  // [8][GP][8]
+    bf16_t *ws = (bf16_t *)(lds_b + P::WOFF);  // [K][64][WR]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int i = lane & 15;
+    const int nseg = (W + kSegB - 1) / kSegB;
+    int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int w0 = (L % nseg) * kSegB;
+    L /= nseg;
+    const int h = L % H;
+    const int n = L / H;
+    const int HW = H * W;
+    const bf16_t *__restrict__ xn = x + (int64_t)n * C * HW;
+    const bf16_t *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
+
+    // ---- staging: item q = 8 channels (plane q & 7) x 8 pixels (run q >> 3), loaded
+    // as eight 16-byte channel runs and written as eight 16-byte pixel slots; runs
+    // outside the image (W % 8 == 0: wholly in or out) are zero
+    u32x4 xreg[P::XIT][8], greg[8], wreg[P::WIT];
+    auto x_row = [&](int st) { return h + ((st % K) - r) * (1 + 2 * (st / K)); };
+    auto load_stage = [&](int st) {
+        const int hs = x_row(st);
+        if (hs >= 0 && hs < H) {  // workgroup-uniform: otherwise the stage is skipped
+#pragma unroll
+            for (int k = 0; k < P::XIT; ++k) {
+                const int q = tid + 256 * k;
+                const int col = w0 - P::LP + 8 * (q >> 3);
+                const bool ok = q < P::NXI && col >= 0 && col < W;
+                const unsigned off = (unsigned)(8 * (q & 7) * HW + hs * W + (ok ? col : 0));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xreg[k][e] = *(const u32x4 *)(xn + (off + (unsigned)(e * HW)));
+            }
+            const int b = st / K, ki = st % K;
+            const bf16_t *wb = wg + (int64_t)(b * C * KK + ki * K) * C;
+#pragma unroll
+            for (int k = 0; k < P::WIT; ++k) {
+                const int q = tid + 256 * k;  // slot: tap q >> 9, row (q >> 3) & 63, 8 columns
+                const int c = (q >> 3) & 63;
+                wreg[k] = *(const u32x4 *)(wb + (c * KK + (q >> 9)) * C + 8 * (q & 7));
+            }
+        }
+        if (st % K == 0) {  // a new branch: its G row
+            const int col = w0 + 8 * (tid >> 3);
+            const unsigned off = (unsigned)(((1 + st / K) * C + 8 * (tid & 7)) * HW + h * W + (col < W ? col : 0));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) greg[e] = *(const u32x4 *)(gn + (off + (unsigned)(e * HW)));
+        }
+    };
+    auto store_stage = [&](int st) {
+        const int hs = x_row(st);
+        if (hs >= 0 && hs < H) {
+#pragma unroll
+            for (int k = 0; k < P::XIT; ++k) {
+                const int q = tid + 256 * k;
+                const int col = w0 - P::LP + 8 * (q >> 3);
+                if (q < P::NXI) {
+                    bf16_t *d = xs + ((q & 7) * P::XP + 8 * (q >> 3)) * 8;
+                    if (col >= 0 && col < W) {
+                        u32x4 o[8];
+                        transpose8x8_bf16(xreg[k], o);
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) *(u32x4 *)(d + 8 * p) = o[p];
+                    } else {  // a run outside the image reads as zero
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) *(u32x4 *)(d + 8 * p) = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < P::WIT; ++k) {
+                const int q = tid + 256 * k;
+                *(u32x4 *)(ws + ((q >> 9) * 64 + ((q >> 3) & 63)) * P::WR + 8 * (q & 7)) = wreg[k];
+            }
+        }
+        if (st % K == 0) {
+            bf16_t *d = gs + ((tid & 7) * P::GP + 8 * (tid >> 3)) * 8;
+            if (w0 + 8 * (tid >> 3) < W) {
+                u32x4 o[8];
+                transpose8x8_bf16(greg, o);
+#pragma unroll
+                for (int p = 0; p < 8; ++p) *(u32x4 *)(d + 8 * p) = o[p];
+            } else {
+#pragma unroll
+                for (int p = 0; p < 8; ++p) *(u32x4 *)(d + 8 * p) = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    // lane's slots: channel plane 4ks + g, pixel 64*wave + 16pb + i (x: + LP + dc)
+    const bf16_t *x_lane = xs + (g * P::XP + 64 * wave + i + P::LP) * 8;
+    const bf16_t *g_lane = gs + (g * P::GP + 64 * wave + i) * 8;
+    // weight rows 32ks + 8g + 4hh + (i >> 2), columns 16nb + 4(i & 3)
+    const bf16_t *w_lane = ws + (8 * g + (i >> 2)) * P::WR + 4 * (i & 3);
+
+    f32x4 acc[4][4];  // [pb][nb]
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[pb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float gf[4][2][8];  // G_b of the lane's pixels: [pb][ks][e]
+
+    load_stage(0);
+#pragma clang loop unroll(full)
+    for (int st = 0; st < NST; ++st) {
+        const int b = st / K;
+        const int ki = st % K;
+        const int D = 1 + 2 * b;
+        const int hs = h + (ki - r) * D;
+        const bool rok = hs >= 0 && hs < H;
+        if (st > 0) __syncthreads();  // every wave is done reading the previous stage
+        store_stage(st);
+        __syncthreads();
+        if (st + 1 < NST) load_stage(st + 1);
+        if (ki == 0) {
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const u32x4 v = *(const u32x4 *)(g_lane + (4 * ks * P::GP + 16 * pb) * 8);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        gf[pb][ks][2 * m] = __uint_as_float(v[m] << 16);
+                        gf[pb][ks][2 * m + 1] = __uint_as_float(v[m] & 0xffff0000u);
+                    }
+                }
+        }
+        if (rok) {
+#pragma clang loop unroll(full)
+            for (int kj = 0; kj < K; ++kj) {
+                const int dc = (kj - r) * D;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    bf16x8 a[4];
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) {
+                        const u32x4 v = *(const u32x4 *)(x_lane + (4 * ks * P::XP + 16 * pb + dc) * 8);
+                        u16x8 u;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            u[2 * m] = f32_to_bf16_bits(gf[pb][ks][2 * m] * __uint_as_float(v[m] << 16));
+                            u[2 * m + 1] = f32_to_bf16_bits(gf[pb][ks][2 * m + 1] * __uint_as_float(v[m] & 0xffff0000u));
+                        }
+                        a[pb] = __builtin_bit_cast(bf16x8, u);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) {
+                        const bf16_t *wp = w_lane + (kj * 64 + 32 * ks) * P::WR + 16 * nb;
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(wp));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(wp + 4 * P::WR));
+                        const bf16x8 bq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) acc[pb][nb] = mfma_16x16x32_bf16(a[pb], bq, acc[pb][nb]);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- rows 4g + v of block pb are pixels 16pb + 4g + v; columns are output
+    // channels 16nb + i
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+        const int col = w0 + 64 * wave + 16 * pb + 4 * g;
+        if (col < W) {  // W % 8 == 0: runs of four are whole
+            bf16_t *yo = gy + (int64_t)n * C * HW + h * W + col;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                u16x4 o;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_bits(acc[pb][nb][v]);
+                *(u16x4 *)(yo + (16 * nb + i) * HW) = o;
+            }
+        }
+    }
+}
+
 }  // namespace
 
-// Applicability: float32, C = 64, W % 4 == 0, 16-byte aligned tensors (checked by
-// the caller) and plane offsets within 32 bits.
-bool bwd_dy_rows_applies(int C, int H, int W, bool al) {
-    return C == kChY && al && (W % 4) == 0 && (int64_t)4 * kChY * H * W < (int64_t(1) << 31);
+// Applicability: C = 64, 16-byte aligned tensors (checked by the caller), W % 4 == 0
+// (float32) or W % 8 == 0 (bfloat16), and plane offsets within 32 bits.
+bool bwd_dy_rows_applies(int C, int H, int W, bool al, bool bf16) {
+    return C == kChY && al && (W % (bf16 ? 8 : 4)) == 0 && (int64_t)4 * kChY * H * W < (int64_t(1) << 31);
+}
+
+int64_t bwd_dy_rows_blocks(int N, int H, int W, bool bf16) {
+    const int seg = bf16 ? kSegB : kSegY;
+    return (int64_t)N * H * ((W + seg - 1) / seg);
+}
+
+template <int K>
+static hipError_t launch_dy_bf16(dim3 grid, const void *x, const void *wg, const void *gout, void *gy, int H, int W,
+                                 hipStream_t stream) {
+    constexpr int lds = DyPlanB<K>::LDS;
+    auto kern = bwd_dy_bf16_kernel<K>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, (const bf16_t *)x, (const bf16_t *)wg, (const bf16_t *)gout,
+                       (bf16_t *)gy, H, W);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_dy_rows(const void *x, const void *wg, const void *gout, void *gy, int N, int H, int W, int K,
-                              hipStream_t stream) {
-    const int64_t nblk = (int64_t)N * H * ((W + kSegY - 1) / kSegY);
+                              bool bf16, hipStream_t stream) {
+    const int64_t nblk = bwd_dy_rows_blocks(N, H, W, bf16);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nblk), block(256);
+    if (bf16) {
+        switch (K) {
+            case 1: return launch_dy_bf16<1>(grid, x, wg, gout, gy, H, W, stream);
+            case 3: return launch_dy_bf16<3>(grid, x, wg, gout, gy, H, W, stream);
+            default: return launch_dy_bf16<5>(grid, x, wg, gout, gy, H, W, stream);
+        }
+    }
     const float *X = (const float *)x, *Wg = (const float *)wg, *G = (const float *)gout;
     float *GY = (float *)gy;
     switch (K) {

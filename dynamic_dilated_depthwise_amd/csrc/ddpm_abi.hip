@@ -97,10 +97,12 @@ int ddpm_filter_fwd(const void *x, const void *taps, void *out, int64_t N, int64
     if (overlaps(out, N * 4 * C * HW * es, x, N * C * HW * es) || overlaps(out, N * 4 * C * HW * es, taps, N * R * HW * es))
         return DDPM_ERR_INVALID_ARG;
     const bool bf16 = dtype == DDPM_BF16;
-    // Runs of 4 pixels in both dtypes: for bfloat16 the 64-lane, 4-row tiles this gives
-    // stream faster than 8-pixel runs (measured 48 vs 56 us at 1x64x256x256).
+    // Runs of 4 pixels (16-byte float32 / 8-byte bfloat16 tap loads).  bfloat16 rows
+    // of 256 pixels or more take runs of 8 (16-byte loads): measured 5.24 vs 5.07 TB/s
+    // at 1x64x256x256, while at 128x128 the taller tiles they imply halve the
+    // workgroup count and lose (3.77 vs 4.01 TB/s).
     int vec = 1;
-    for (int v = 4; v > 1; v /= 2) {
+    for (int v = bf16 && W >= 256 ? 8 : 4; v > 1; v /= 2) {
         const uintptr_t al = (uintptr_t)v * es;
         if (W % v == 0 && (uintptr_t)x % al == 0 && (uintptr_t)taps % al == 0 && (uintptr_t)out % al == 0) {
             vec = v;

@@ -9,10 +9,13 @@
 //   * one workgroup = one (n, c) plane x a TH x TW pixel tile;
 //   * the x tile plus a 5*(K-1)/2 halo is staged once in LDS (as float), so every
 //     dilation's neighbourhood is read from LDS, never re-fetched from HBM;
-//   * each thread owns VEC = 4 consecutive pixels of a row (16-byte float32 /
-//     8-byte bfloat16 runs) and streams the taps with non-temporal vector loads
-//     (they are touched exactly once), and writes the four output planes with
-//     non-temporal vector stores;
+//   * each thread owns VEC consecutive pixels of a row (4 float32 or 4-8 bfloat16)
+//     and streams the taps with non-temporal vector loads (they are touched
+//     exactly once), and writes the four output planes with non-temporal vector
+//     stores;
+//   * for runs of 4 or more the staged x row of each row offset is read once as
+//     aligned 16-byte LDS words, and every tap of that offset picks its values out
+//     of those registers (fewer, conflict-free LDS reads than one read per tap);
 //   * the x block of the output is copied from the staged tile bit-exactly.
 #include "common.hpp"
 #include "launchers.hpp"
@@ -62,19 +65,66 @@ __global__ __launch_bounds__(256) void filter_fwd_kernel(const T *__restrict__ x
 
         float acc[3][VEC];
 #pragma unroll
-        for (int b = 0; b < 3; ++b) {
-            const int D = dilation(b);
+        for (int b = 0; b < 3; ++b)
 #pragma unroll
             for (int k = 0; k < VEC; ++k) acc[b][k] = 0.f;
+        if constexpr (VEC >= 4) {
+            // The taps of one row offset dr = (ki - r) * D read one staged row: it is
+            // loaded once as aligned 16-byte runs covering columns lc - PADC ..
+            // lc + VEC - 1 + PADC, and each tap takes its VEC values from the window at
+            // a compile-time position.
+            constexpr int NWIN = VEC / 4 + PADC / 2;  // 16-byte runs in the window
+            V tv[3][KK];
 #pragma unroll
-            for (int t = 0; t < KK; ++t) {
-                const int ki = t / K, kj = t % K;
-                const int64_t plane = (int64_t)(b * C + c) * KK + t;
-                const V tv = __builtin_nontemporal_load((const V *)(tp + plane * HW + pix));
-                const float *xn = xc + (ki - r) * D * LW + (kj - r) * D;
+            for (int b = 0; b < 3; ++b)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    acc[b][k] += Elem<T>::to_f32(lane_of<V, T, VEC>(tv, k)) * xn[k];
+                for (int t = 0; t < KK; ++t)
+                    tv[b][t] = __builtin_nontemporal_load(
+                        (const V *)(tp + ((int64_t)(b * C + c) * KK + t) * HW + pix));
+            const float *xw = xs + (lr + HALO) * LW + lc;  // window column 0 = pixel lc - PADC
+#pragma unroll
+            for (int dr = -HALO; dr <= HALO; ++dr) {
+                bool used = false;
+#pragma unroll
+                for (int b = 0; b < 3; ++b)
+#pragma unroll
+                    for (int ki = 0; ki < K; ++ki) used = used || (ki - r) * dilation(b) == dr;
+                if (!used) continue;
+                float win[4 * NWIN];
+#pragma unroll
+                for (int q = 0; q < NWIN; ++q) {
+                    const f32x4 v = *(const f32x4 *)(xw + dr * LW + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) win[4 * q + e] = v[e];
+                }
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    const int D = dilation(b);
+#pragma unroll
+                    for (int t = 0; t < KK; ++t) {
+                        const int ki = t / K, kj = t % K;
+                        if ((ki - r) * D != dr) continue;
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k)
+                            acc[b][k] += Elem<T>::to_f32(lane_of<V, T, VEC>(tv[b][t], k)) *
+                                         win[PADC + (kj - r) * D + k];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 3; ++b) {
+                const int D = dilation(b);
+#pragma unroll
+                for (int t = 0; t < KK; ++t) {
+                    const int ki = t / K, kj = t % K;
+                    const int64_t plane = (int64_t)(b * C + c) * KK + t;
+                    const V tv = __builtin_nontemporal_load((const V *)(tp + plane * HW + pix));
+                    const float *xn = xc + (ki - r) * D * LW + (kj - r) * D;
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k)
+                        acc[b][k] += Elem<T>::to_f32(lane_of<V, T, VEC>(tv, k)) * xn[k];
+                }
             }
         }
         V xv;
@@ -131,6 +181,9 @@ template <typename T, int K>
 static hipError_t launch_filter_k(const void *x, const void *taps, void *out, int N, int C, int H, int W,
                                   hipStream_t stream, int vec) {
     switch (vec) {
+        case 8:
+            if constexpr (Elem<T>::is_bf16) return launch_filter_t<T, K, 8>(x, taps, out, N, C, H, W, stream);
+            return hipErrorInvalidValue;
         case 4: return launch_filter_t<T, K, 4>(x, taps, out, N, C, H, W, stream);
         case 2: return launch_filter_t<T, K, 2>(x, taps, out, N, C, H, W, stream);
         default: return launch_filter_t<T, K, 1>(x, taps, out, N, C, H, W, stream);

@@ -31,11 +31,12 @@ bool bwd_dx_rows_applies(int C, int H, int W, bool al);
 hipError_t launch_bwd_dx_rows(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
                               int H, int W, int K, bool bf16, hipStream_t stream);
 
-// dY in float32 for C = 64 staged by source row; bwd_dy_rows_applies tells whether
-// a shape can take it.
-bool bwd_dy_rows_applies(int C, int H, int W, bool al);
+// dY for C = 64 staged by source row (both dtypes); bwd_dy_rows_applies tells
+// whether a shape can take it, bwd_dy_rows_blocks gives its grid size.
+bool bwd_dy_rows_applies(int C, int H, int W, bool al, bool bf16);
+int64_t bwd_dy_rows_blocks(int N, int H, int W, bool bf16);
 hipError_t launch_bwd_dy_rows(const void *x, const void *wg, const void *gout, void *gy, int N, int H, int W, int K,
-                              hipStream_t stream);
+                              bool bf16, hipStream_t stream);
 
 // gx or gtaps may be null: that output is skipped (not both).
 hipError_t launch_filter_bwd(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N, int C,

@@ -21,7 +21,10 @@ DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("name,shape", [("nonaligned_k3", synth.Shape(2, 24, 15, 17, 3)),
-                                        ("c64_k5", synth.Shape(1, 64, 20, 72, 5))], ids=["nonaligned_k3", "c64_k5"])
+                                        ("c64_k5", synth.Shape(1, 64, 20, 72, 5)),
+                                        # the row-staged backward kernels and 8-pixel filter runs
+                                        ("c64_256", synth.Shape(1, 64, 256, 256, 3))],
+                         ids=["nonaligned_k3", "c64_k5", "c64_256"])
 def test_graph_replays_match_eager(name, shape, dt):
     dtype = DT[dt]
     K = shape.K

@@ -39,6 +39,8 @@ FWD_CASES = [
     ("c48_ragged", (S_(1, 48, 12, 70, 3), 113)), ("c64_w200_k5", (S_(1, 64, 9, 200, 5), 114)),
     # rows wider than one tile (several column tiles; the checked backward dX path)
     ("w520_wide", (S_(1, 4, 6, 520, 3), 115)), ("w1030_k5", (S_(1, 3, 5, 1030, 5), 116)),
+    # rows of 256+ pixels with W % 8 == 0 (8-pixel bfloat16 runs) at K = 5 and K = 1
+    ("w256_k5", (S_(1, 6, 13, 256, 5), 118)), ("w264_k1", (S_(2, 5, 3, 264, 1), 119)),
     # a batch of four mid-size images on the workload's channel count (full-size grids)
     ("batch4_c64_64", (S_(4, 64, 64, 64, 3), 117)),
 ]
@@ -63,6 +65,11 @@ BWD_CASES = [
     # segment per row, and K = 5 with a ragged 200-column row and 130 rows
     ("c64_w100_batch2", (S_(2, 64, 160, 100, 3), 220)), ("c64_k1_tall", (S_(1, 64, 520, 64, 1), 221)),
     ("c64_k5_w200", (S_(1, 64, 130, 200, 5), 222)),
+    # C = 64 grids of at least one 256-pixel segment per CU (the row-staged bf16 dY):
+    # K = 5 on a ragged 200-column row, two segments (256 + 8 columns), and a batch of
+    # two at K = 1 with a ragged 136-column row
+    ("c64_k5_w200_tall", (S_(1, 64, 264, 200, 5), 223)), ("c64_w264_two_seg", (S_(1, 64, 130, 264, 3), 224)),
+    ("c64_k1_batch2_w136", (S_(2, 64, 128, 136, 1), 225)),
 ]
 
 
