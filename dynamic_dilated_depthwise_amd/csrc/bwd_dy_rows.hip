@@ -255,7 +255,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
 
 
 // ============================================================================ bfloat16
-constexpr int kSegB = 256;  // pixels per workgroup (four waves x 64)
+constexpr int kSegB = 256;  // pixels per workgroup
+constexpr int kPxB = 32;    // pixels per wave (two MFMA row blocks)
+constexpr int kWavesB = kSegB / kPxB;
+constexpr int kThreadsB = 64 * kWavesB;
 
 template <int K> struct DyPlanB {
     static constexpr int r = (K - 1) / 2;
@@ -270,8 +273,9 @@ template <int K> struct DyPlanB {
     static constexpr int GP = kSegB + 1;
     static constexpr int WR = 80;                // bf16 elements per staged weight row (64 + pad)
     static constexpr int NXI = XS;               // x items (8 channels x 8 pixels): 8 planes x XS/8
-    static constexpr int XIT = (NXI + 255) / 256;
-    static constexpr int WIT = 2 * K;            // 16-byte weight slots per thread per stage
+    static constexpr int XIT = (NXI + kThreadsB - 1) / kThreadsB;
+    static constexpr int NGI = kSegB;            // G items, taken by the last 256 threads
+    static constexpr int WIT = 512 * K / kThreadsB;  // 16-byte weight slots per thread per stage
     static constexpr int XOFF = 0;               // byte offsets of the LDS regions
     static constexpr int GOFF = XOFF + 8 * XP * 16;
     static constexpr int WOFF = GOFF + 8 * GP * 16;
@@ -296,7 +300,7 @@ __device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&u)[8], u32x4 (&o
 }
 
 template <int K>
-__global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__restrict__ x,
+__global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t *__restrict__ x,
                                                              const bf16_t *__restrict__ wg,
                                                              const bf16_t *__restrict__ gout,
                                                              bf16_t *__restrict__ gy, int H, int W) {
@@ -329,13 +333,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
     // as eight 16-byte channel runs and written as eight 16-byte pixel slots; runs
     // outside the image (W % 8 == 0: wholly in or out) are zero
     u32x4 xreg[P::XIT][8], greg[8], wreg[P::WIT];
+    const int qg = tid - (kThreadsB - P::NGI);  // G item of this thread (the last 256 threads)
     auto x_row = [&](int st) { return h + ((st % K) - r) * (1 + 2 * (st / K)); };
     auto load_stage = [&](int st) {
         const int hs = x_row(st);
         if (hs >= 0 && hs < H) {  // workgroup-uniform: otherwise the stage is skipped
 #pragma unroll
             for (int k = 0; k < P::XIT; ++k) {
-                const int q = tid + 256 * k;
+                const int q = tid + kThreadsB * k;
                 const int col = w0 - P::LP + 8 * (q >> 3);
                 const bool ok = q < P::NXI && col >= 0 && col < W;
                 const unsigned off = (unsigned)(8 * (q & 7) * HW + hs * W + (ok ? col : 0));
@@ -346,14 +351,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
             const bf16_t *wb = wg + (int64_t)(b * C * KK + ki * K) * C;
 #pragma unroll
             for (int k = 0; k < P::WIT; ++k) {
-                const int q = tid + 256 * k;  // slot: tap q >> 9, row (q >> 3) & 63, 8 columns
+                const int q = tid + kThreadsB * k;  // slot: tap q >> 9, row (q >> 3) & 63, 8 columns
                 const int c = (q >> 3) & 63;
                 wreg[k] = *(const u32x4 *)(wb + (c * KK + (q >> 9)) * C + 8 * (q & 7));
             }
         }
-        if (st % K == 0) {  // a new branch: its G row
-            const int col = w0 + 8 * (tid >> 3);
-            const unsigned off = (unsigned)(((1 + st / K) * C + 8 * (tid & 7)) * HW + h * W + (col < W ? col : 0));
+        if (st % K == 0 && qg >= 0) {  // a new branch: its G row
+            const int col = w0 + 8 * (qg >> 3);
+            const unsigned off = (unsigned)(((1 + st / K) * C + 8 * (qg & 7)) * HW + h * W + (col < W ? col : 0));
 #pragma unroll
             for (int e = 0; e < 8; ++e) greg[e] = *(const u32x4 *)(gn + (off + (unsigned)(e * HW)));
         }
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
         if (hs >= 0 && hs < H) {
 #pragma unroll
             for (int k = 0; k < P::XIT; ++k) {
-                const int q = tid + 256 * k;
+                const int q = tid + kThreadsB * k;
                 const int col = w0 - P::LP + 8 * (q >> 3);
                 if (q < P::NXI) {
                     bf16_t *d = xs + ((q & 7) * P::XP + 8 * (q >> 3)) * 8;
@@ -380,13 +385,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
             }
 #pragma unroll
             for (int k = 0; k < P::WIT; ++k) {
-                const int q = tid + 256 * k;
+                const int q = tid + kThreadsB * k;
                 *(u32x4 *)(ws + ((q >> 9) * 64 + ((q >> 3) & 63)) * P::WR + 8 * (q & 7)) = wreg[k];
             }
         }
-        if (st % K == 0) {
-            bf16_t *d = gs + ((tid & 7) * P::GP + 8 * (tid >> 3)) * 8;
-            if (w0 + 8 * (tid >> 3) < W) {
+        if (st % K == 0 && qg >= 0) {
+            bf16_t *d = gs + ((qg & 7) * P::GP + 8 * (qg >> 3)) * 8;
+            if (w0 + 8 * (qg >> 3) < W) {
                 u32x4 o[8];
                 transpose8x8_bf16(greg, o);
 #pragma unroll
@@ -398,18 +403,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
         }
     };
 
-    // lane's slots: channel plane 4ks + g, pixel 64*wave + 16pb + i (x: + LP + dc)
-    const bf16_t *x_lane = xs + (g * P::XP + 64 * wave + i + P::LP) * 8;
-    const bf16_t *g_lane = gs + (g * P::GP + 64 * wave + i) * 8;
+    constexpr int NPB = kPxB / 16;
+    // lane's slots: channel plane 4ks + g, pixel kPxB*wave + 16pb + i (x: + LP + dc)
+    const bf16_t *x_lane = xs + (g * P::XP + kPxB * wave + i + P::LP) * 8;
+    const bf16_t *g_lane = gs + (g * P::GP + kPxB * wave + i) * 8;
     // weight rows 32ks + 8g + 4hh + (i >> 2), columns 16nb + 4(i & 3)
     const bf16_t *w_lane = ws + (8 * g + (i >> 2)) * P::WR + 4 * (i & 3);
 
-    f32x4 acc[4][4];  // [pb][nb]
+    f32x4 acc[NPB][4];  // [pb][nb]
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[pb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float gf[4][2][8];  // G_b of the lane's pixels: [pb][ks][e]
+    float gf[NPB][2][8];  // G_b of the lane's pixels: [pb][ks][e]
 
     load_stage(0);
 #pragma clang loop unroll(full)
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
         if (st + 1 < NST) load_stage(st + 1);
         if (ki == 0) {
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb)
+            for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const u32x4 v = *(const u32x4 *)(g_lane + (4 * ks * P::GP + 16 * pb) * 8);
@@ -442,9 +448,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
                 const int dc = (kj - r) * D;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    bf16x8 a[4];
+                    bf16x8 a[NPB];
 #pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) {
+                    for (int pb = 0; pb < NPB; ++pb) {
                         const u32x4 v = *(const u32x4 *)(x_lane + (4 * ks * P::XP + 16 * pb + dc) * 8);
                         u16x8 u;
 #pragma unroll
@@ -461,7 +467,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
                         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(wp + 4 * P::WR));
                         const bf16x8 bq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-                        for (int pb = 0; pb < 4; ++pb) acc[pb][nb] = mfma_16x16x32_bf16(a[pb], bq, acc[pb][nb]);
+                        for (int pb = 0; pb < NPB; ++pb) acc[pb][nb] = mfma_16x16x32_bf16(a[pb], bq, acc[pb][nb]);
                     }
                 }
             }
@@ -471,8 +477,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dy_bf16_kernel(const bf16_t *__res
     // ---- rows 4g + v of block pb are pixels 16pb + 4g + v; columns are output
     // channels 16nb + i
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-        const int col = w0 + 64 * wave + 16 * pb + 4 * g;
+    for (int pb = 0; pb < NPB; ++pb) {
+        const int col = w0 + kPxB * wave + 16 * pb + 4 * g;
         if (col < W) {  // W % 8 == 0: runs of four are whole
             bf16_t *yo = gy + (int64_t)n * C * HW + h * W + col;
 #pragma unroll
@@ -506,7 +512,7 @@ static hipError_t launch_dy_bf16(dim3 grid, const void *x, const void *wg, const
     auto kern = bwd_dy_bf16_kernel<K>;
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, (const bf16_t *)x, (const bf16_t *)wg, (const bf16_t *)gout,
+    hipLaunchKernelGGL(kern, grid, dim3(kThreadsB), lds, stream, (const bf16_t *)x, (const bf16_t *)wg, (const bf16_t *)gout,
                        (bf16_t *)gy, H, W);
     return hipGetLastError();
 }
