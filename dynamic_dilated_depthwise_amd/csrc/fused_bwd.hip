@@ -623,8 +623,11 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // dW / db partials
-    if (dwp != nullptr) {
+    // dW / db partials (C = 64: staged by row segment, bwd_dw_rows.hip)
+    if (dwp != nullptr && bwd_dw_rows_applies(C, H, W, al, BF)) {
+        hipError_t e = launch_bwd_dw_rows(x, y, gout, dwp, dbp, S, N, H, W, K, BF, stream);
+        if (e != hipSuccess) return e;
+    } else if (dwp != nullptr) {
         const dim3 grid((unsigned)nblk_dw);
         const int nb = (C >= 64) ? 4 : (C + 15) / 16;
         auto args = [&](auto kern) {

@@ -38,6 +38,12 @@ int64_t bwd_dy_rows_blocks(int N, int H, int W, bool bf16);
 hipError_t launch_bwd_dy_rows(const void *x, const void *wg, const void *gout, void *gy, int N, int H, int W, int K,
                               bool bf16, hipStream_t stream);
 
+// dW / db partials for C = 64 staged by row segment (both dtypes); the grid and
+// token ranges are those of the general kernel.
+bool bwd_dw_rows_applies(int C, int H, int W, bool al, bool bf16);
+hipError_t launch_bwd_dw_rows(const void *x, const void *y, const void *gout, float *dw_part, float *db_part, int S,
+                              int N, int H, int W, int K, bool bf16, hipStream_t stream);
+
 // gx or gtaps may be null: that output is skipped (not both).
 hipError_t launch_filter_bwd(const void *x, const void *taps, const void *gout, void *gx, void *gtaps, int N, int C,
                              int H, int W, int K, bool bf16, int vec, bool aligned, hipStream_t stream);

@@ -123,6 +123,42 @@ def test_weight_gradient_rounds_dk_bias_gradient_does_not(seed):
         assert want_w != other_w and want_b != other_b, "case does not separate the readings"
 
 
+@pytest.mark.parametrize("seed", [33, 34])
+def test_weight_gradient_rounding_c64(seed):
+    """The same two readings at C = 64 (the segment-staged partial kernel): with
+    K = 1, dW[(b, c), c'] = sum_p rne(G_b[c, p] x[c, p]) y[c', p] and
+    db[(b, c)] = sum_p G_b[c, p] x[c, p], over 2 x 16 pixels.  The grid values keep
+    every product and partial sum exact in float32 whatever the summation order."""
+    C, H, W = 64, 2, 16
+    x = _grid_values((1, C, H, W), seed)
+    y = _grid_values((1, C, H, W), seed + 1)
+    gout = _grid_values((1, 4 * C, H, W), seed + 2)
+    w = _draw((3 * C, C), seed + 3, 0.1)
+    b = _draw((3 * C,), seed + 4, 0.3)
+    pw = torch.empty((1, 3 * C, C), device="cuda", dtype=torch.float32)
+    pb = torch.empty((1, 3 * C), device="cuda", dtype=torch.float32)
+    ddpm.ddpm_fused_bwd(x.cuda(), y.cuda(), w.cuda(), b.cuda(), gout.cuda(), None, None, pw, pb, 1)
+    torch.cuda.synchronize()
+    xv = x.float().numpy()[0].reshape(C, -1)
+    yv = y.float().numpy()[0].reshape(C, -1).astype(np.float64)
+    gv = gout.float().numpy()[0].reshape(4 * C, -1)
+    got_w, got_b = pw[0].cpu().numpy(), pb[0].cpu().numpy()
+    separated_w = separated_b = False
+    for k in range(3):
+        dk = (gv[(1 + k) * C:(2 + k) * C] * xv).astype(np.float32)  # exact, [c, p]
+        want_w = (_rne(dk).astype(np.float64) @ yv.T).astype(np.float32)  # [c, c']
+        want_b = dk.astype(np.float64).sum(1).astype(np.float32)
+        other_w = (dk.astype(np.float64) @ yv.T).astype(np.float32)
+        other_b = _rne(dk).astype(np.float64).sum(1).astype(np.float32)
+        bad_w = int((got_w[k * C:(k + 1) * C] != want_w).sum())
+        bad_b = int((got_b[k * C:(k + 1) * C] != want_b).sum())
+        assert bad_w == 0, f"branch {k}: {bad_w} dW elements differ from sum rne(dK) y"
+        assert bad_b == 0, f"branch {k}: {bad_b} db elements differ from sum dK"
+        separated_w = separated_w or bool((want_w != other_w).any())
+        separated_b = separated_b or bool((want_b != other_b).any())
+    assert separated_w and separated_b, "case does not separate the readings"
+
+
 @pytest.mark.parametrize("seed", [41, 42])
 def test_fused_dy_rounds_dk(seed):
     """dY = W^T rne(dK): with K = 1 and one channel, dY = rne(sum_b W_b rne(G_b x)).

@@ -214,11 +214,14 @@ def test_misaligned_pointers(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [S_(2, 24, 15, 17, 3), S_(1, 16, 20, 64, 3)], ids=["w17", "w64"])
+@pytest.mark.parametrize("shape", [S_(2, 24, 15, 17, 3), S_(1, 16, 20, 64, 3), S_(1, 64, 20, 72, 3)],
+                         ids=["w17", "w64", "c64_w72"])
 @pytest.mark.parametrize("S", [1, 3, 7, 16])
 def test_partial_counts_agree(S, shape, dt):
     """Any split count gives the same reduced gradients.  With W = 64 the split
-    boundaries fall at odd and even columns of aligned rows (vector run paths)."""
+    boundaries fall at odd and even columns of aligned rows (vector run paths); with
+    C = 64 and W = 72 the segment-staged kernel walks ranges that start mid-row and
+    rows that end in a partial segment."""
     dtype = DT[dt]
     h = inputs(shape, 302, dtype, grad=True)
     a = {k: f64(v) for k, v in h.items()}
@@ -234,14 +237,16 @@ def test_partial_counts_agree(S, shape, dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_partials_follow_documented_ranges(dt):
+@pytest.mark.parametrize("shape", [S_(1, 8, 37, 45, 3), S_(1, 64, 37, 48, 3)], ids=["c8", "c64"])
+def test_partials_follow_documented_ranges(shape, dt):
     """Each partial holds the sum over the token range the header documents: range s
     starts at floor(T*s/S) rounded down to 64 (float32) / 128 (bfloat16) tokens and
     the last ends at T.  The expected partial s is the oracle's gradient with
     grad_out zeroed outside range s (a token's dK, hence its contribution, is
-    proportional to grad_out at that token)."""
+    proportional to grad_out at that token).  C = 64 takes the segment-staged
+    kernel."""
     dtype = DT[dt]
-    shape, S = S_(1, 8, 37, 45, 3), 5
+    S = 5
     K, T = shape.K, shape.N * shape.H * shape.W
     h = inputs(shape, 303, dtype, grad=True)
     a = {k: f64(v) for k, v in h.items()}
