@@ -470,7 +470,9 @@ hipError_t launch_dx_t(const void *y, const void *wg, const void *bg, const void
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), 0, stream, (const T *)y, (const T *)wg,
                            (const T *)bg, (const T *)gout, (T *)gx, C, H, W, al ? 1 : 0);
     };
-    if (nblk > 2 * kCUs && bwd_dx_rows_applies(C, H, W, al))
+    // row-staged kernel from one 64-pixel segment per CU up (measured at 128x128,
+    // C = 64: K = 5 bf16 140 -> 55 us, fp32 146 -> 108 us; K = 3 bf16 60 -> 28 us)
+    if (nblk >= kCUs && bwd_dx_rows_applies(C, H, W, al))
         return launch_bwd_dx_rows(y, wg, bg, gout, gx, N, H, W, K, Elem<T>::is_bf16, stream);
     if (nblk <= kCUs) {
         if (fullw) launch(bwd_dx_kernel<T, K, 4, !Elem<T>::is_bf16>, 1024);

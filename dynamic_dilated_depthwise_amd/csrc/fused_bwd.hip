@@ -586,12 +586,10 @@ static hipError_t launch_bwd_k(const void *x, const void *y, const void *wg, con
         hipError_t e = launch_bwd_dx(y, wg, bg, gout, gx, N, C, H, W, K, Elem<T>::is_bf16, al, stream);
         if (e != hipSuccess) return e;
     }
-    // dY staged by source row (bwd_dy_rows.hip) for C = 64 when its grid fills the
-    // chip: float32 more than two 64-pixel segments per CU, bfloat16 at least one
-    // 256-pixel segment per CU
+    // dY staged by source row (bwd_dy_rows.hip) for C = 64 when its grid gives at
+    // least one row segment (64 pixels float32, 256 bfloat16) per CU
     constexpr bool BF = Elem<T>::is_bf16;
-    if (gy != nullptr && bwd_dy_rows_applies(C, H, W, al, BF) &&
-        bwd_dy_rows_blocks(N, H, W, BF) >= (BF ? kCUs : 2 * kCUs + 1)) {
+    if (gy != nullptr && bwd_dy_rows_applies(C, H, W, al, BF) && bwd_dy_rows_blocks(N, H, W, BF) >= kCUs) {
         hipError_t e = launch_bwd_dy_rows(x, wg, gout, gy, N, H, W, K, BF, stream);
         if (e != hipSuccess) return e;
     } else if (gy != nullptr) {
