@@ -25,10 +25,11 @@
 //
 // bfloat16 (bwd_dy_bf16_kernel): one MFMA k-step covers 32 input channels, so the
 // waves split pixels instead and each forms dK only for its own pixels, once:
-// workgroup = one 256-pixel row segment, wave v = pixels 64v .. 64v+63 x all 64
-// output channels (v_mfma_f32_16x16x32_bf16):
-//   rows    = 16 pixels 16pb + i of the wave (four blocks pb);
-//   columns = 16 output channels 16nb + j (four blocks nb);
+// workgroup = one 256-pixel row segment, wave v = pixels 32v .. 32v+31 x all 64
+// output channels (for small grids: one 128-pixel segment x 32 output channels, the
+// segment's two halves in neighbouring workgroups) (v_mfma_f32_16x16x32_bf16):
+//   rows    = 16 pixels 16pb + i of the wave (two blocks pb);
+//   columns = 16 output channels 16nb + j (four blocks nb, two when split);
 //   k       = 32 input channels 32ks + 8g + e (two k-steps ks).
 // x and G_b are staged as [channel/8][pixel][8] so that a lane's eight channels of
 // one pixel are one 16-byte LDS read at any column shift; each wave keeps its
@@ -255,27 +256,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
 
 
 // ============================================================================ bfloat16
-constexpr int kSegB = 256;  // pixels per workgroup
 constexpr int kPxB = 32;    // pixels per wave (two MFMA row blocks)
-constexpr int kWavesB = kSegB / kPxB;
-constexpr int kThreadsB = 64 * kWavesB;
 
-template <int K> struct DyPlanB {
+// SEG pixels per workgroup (SEG / 32 waves), NCP of the 64 output channels per
+// workgroup (64, or 32 with the two halves in neighbouring workgroups, for grids
+// that are otherwise too small: each half forms the segment's dK itself).
+template <int K, int SEG, int NCP> struct DyPlanB {
+    static constexpr int WAVES = SEG / kPxB;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int NB = NCP / 16;          // output-channel blocks per wave
     static constexpr int r = (K - 1) / 2;
     static constexpr int KK = K * K;
     static constexpr int NST = 3 * K;            // (branch, kernel row) stages, branch-major
     static constexpr int HALO = 5 * r;
     static constexpr int LP = (HALO + 7) & ~7;   // staged x pixels left of the segment (8-pixel runs)
-    static constexpr int XS = kSegB + 2 * LP;    // staged x pixels
+    static constexpr int XS = SEG + 2 * LP;      // staged x pixels
     // 16-byte slots per channel-group plane: one more than a multiple of 16, so the
     // staging writes of 16 consecutive lanes (8 planes x 2 runs) hit distinct banks
     static constexpr int XP = (XS + 15) / 16 * 16 + 1;
-    static constexpr int GP = kSegB + 1;
-    static constexpr int WR = 80;                // bf16 elements per staged weight row (64 + pad)
+    static constexpr int GP = SEG + 1;
+    static constexpr int WR = NCP + 16;          // bf16 elements per staged weight row (NCP + pad)
+    static constexpr int WSR = NCP / 8;          // 16-byte weight slots per row
     static constexpr int NXI = XS;               // x items (8 channels x 8 pixels): 8 planes x XS/8
-    static constexpr int XIT = (NXI + kThreadsB - 1) / kThreadsB;
-    static constexpr int NGI = kSegB;            // G items, taken by the last 256 threads
-    static constexpr int WIT = 512 * K / kThreadsB;  // 16-byte weight slots per thread per stage
+    static constexpr int XIT = (NXI + THREADS - 1) / THREADS;
+    static constexpr int NGI = SEG;              // G items, taken by the last SEG threads
+    static constexpr int WIT = K * 64 * WSR / THREADS;  // 16-byte weight slots per thread per stage
+    static_assert(K * 64 * WSR % THREADS == 0, "whole weight slots per thread");
     static constexpr int XOFF = 0;               // byte offsets of the LDS regions
     static constexpr int GOFF = XOFF + 8 * XP * 16;
     static constexpr int WOFF = GOFF + 8 * GP * 16;
@@ -299,29 +305,34 @@ __device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&u)[8], u32x4 (&o
                                             (k & 1) ? 0x07060302u : 0x05040100u);
 }
 
-template <int K>
-__global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t *__restrict__ x,
+template <int K, int SEG, int NCP>
+__global__ __launch_bounds__((DyPlanB<K, SEG, NCP>::THREADS), 1) void bwd_dy_bf16_kernel(const bf16_t *__restrict__ x,
                                                              const bf16_t *__restrict__ wg,
                                                              const bf16_t *__restrict__ gout,
                                                              bf16_t *__restrict__ gy, int H, int W) {
-    using P = DyPlanB<K>;
+    using P = DyPlanB<K, SEG, NCP>;
     constexpr int r = P::r;
     constexpr int KK = P::KK;
     constexpr int NST = P::NST;
     constexpr int C = kChY;
+    constexpr int kThreadsB = P::THREADS;
+    constexpr int NB = P::NB;
     extern __shared__ __align__(16) unsigned char lds_b[];
     bf16_t *xs = (bf16_t *)(lds_b + P::XOFF);  // [8][XP][8]
     bf16_t *gs = (bf16_t *)(lds_b + P::GOFF);  // [8][GP][8]
-    bf16_t *ws = (bf16_t *)(lds_b + P::WOFF);  // [K][64][WR]
+    bf16_t *ws = (bf16_t *)(lds_b + P::WOFF);  // [K][64][WR]: columns cp0 .. cp0 + NCP - 1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int i = lane & 15;
-    const int nseg = (W + kSegB - 1) / kSegB;
+    constexpr int NSPL = 64 / NCP;
+    const int nseg = (W + SEG - 1) / SEG;
     int L = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int w0 = (L % nseg) * kSegB;
+    const int cp0 = (L % NSPL) * NCP;  // the workgroup's output channels (halves of a segment are neighbours)
+    L /= NSPL;
+    const int w0 = (L % nseg) * SEG;
     L /= nseg;
     const int h = L % H;
     const int n = L / H;
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t 
     // as eight 16-byte channel runs and written as eight 16-byte pixel slots; runs
     // outside the image (W % 8 == 0: wholly in or out) are zero
     u32x4 xreg[P::XIT][8], greg[8], wreg[P::WIT];
-    const int qg = tid - (kThreadsB - P::NGI);  // G item of this thread (the last 256 threads)
+    const int qg = tid - (kThreadsB - P::NGI);  // G item of this thread (the last SEG threads)
     auto x_row = [&](int st) { return h + ((st % K) - r) * (1 + 2 * (st / K)); };
     auto load_stage = [&](int st) {
         const int hs = x_row(st);
@@ -351,9 +362,11 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t 
             const bf16_t *wb = wg + (int64_t)(b * C * KK + ki * K) * C;
 #pragma unroll
             for (int k = 0; k < P::WIT; ++k) {
-                const int q = tid + kThreadsB * k;  // slot: tap q >> 9, row (q >> 3) & 63, 8 columns
-                const int c = (q >> 3) & 63;
-                wreg[k] = *(const u32x4 *)(wb + (c * KK + (q >> 9)) * C + 8 * (q & 7));
+                const int q = tid + kThreadsB * k;  // slot: tap, row c, 8 columns
+                const int tap = q / (64 * P::WSR);
+                const int rem = q - tap * 64 * P::WSR;
+                const int c = rem / P::WSR;
+                wreg[k] = *(const u32x4 *)(wb + (c * KK + tap) * C + cp0 + 8 * (rem - c * P::WSR));
             }
         }
         if (st % K == 0 && qg >= 0) {  // a new branch: its G row
@@ -386,7 +399,10 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t 
 #pragma unroll
             for (int k = 0; k < P::WIT; ++k) {
                 const int q = tid + kThreadsB * k;
-                *(u32x4 *)(ws + ((q >> 9) * 64 + ((q >> 3) & 63)) * P::WR + 8 * (q & 7)) = wreg[k];
+                const int tap = q / (64 * P::WSR);
+                const int rem = q - tap * 64 * P::WSR;
+                const int c = rem / P::WSR;
+                *(u32x4 *)(ws + (tap * 64 + c) * P::WR + 8 * (rem - c * P::WSR)) = wreg[k];
             }
         }
         if (st % K == 0 && qg >= 0) {
@@ -410,11 +426,11 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t 
     // weight rows 32ks + 8g + 4hh + (i >> 2), columns 16nb + 4(i & 3)
     const bf16_t *w_lane = ws + (8 * g + (i >> 2)) * P::WR + 4 * (i & 3);
 
-    f32x4 acc[NPB][4];  // [pb][nb]
+    f32x4 acc[NPB][NB];  // [pb][nb]
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[pb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; ++nb) acc[pb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float gf[NPB][2][8];  // G_b of the lane's pixels: [pb][ks][e]
 
     load_stage(0);
@@ -461,7 +477,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t 
                         a[pb] = __builtin_bit_cast(bf16x8, u);
                     }
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
+                    for (int nb = 0; nb < NB; ++nb) {
                         const bf16_t *wp = w_lane + (kj * 64 + 32 * ks) * P::WR + 16 * nb;
                         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(wp));
                         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(wp + 4 * P::WR));
@@ -482,11 +498,11 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dy_bf16_kernel(const bf16_t 
         if (col < W) {  // W % 8 == 0: runs of four are whole
             bf16_t *yo = gy + (int64_t)n * C * HW + h * W + col;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
                 u16x4 o;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_bits(acc[pb][nb][v]);
-                *(u16x4 *)(yo + (16 * nb + i) * HW) = o;
+                *(u16x4 *)(yo + (cp0 + 16 * nb + i) * HW) = o;
             }
         }
     }
@@ -500,21 +516,36 @@ bool bwd_dy_rows_applies(int C, int H, int W, bool al, bool bf16) {
     return C == kChY && al && (W % (bf16 ? 8 : 4)) == 0 && (int64_t)4 * kChY * H * W < (int64_t(1) << 31);
 }
 
+// bfloat16: 256-pixel segments x all 64 output channels when rows are wider than 128
+// pixels and that grid gives every CU a segment; otherwise 128-pixel segments x 32
+// output channels, the two halves of a segment in neighbouring workgroups.
+static bool dy_bf16_wide(int N, int H, int W) {
+    return W > 128 && (int64_t)N * H * ((W + 255) / 256) >= 256;
+}
+
 int64_t bwd_dy_rows_blocks(int N, int H, int W, bool bf16) {
-    const int seg = bf16 ? kSegB : kSegY;
-    return (int64_t)N * H * ((W + seg - 1) / seg);
+    if (!bf16) return (int64_t)N * H * ((W + kSegY - 1) / kSegY);
+    return dy_bf16_wide(N, H, W) ? (int64_t)N * H * ((W + 255) / 256) : (int64_t)N * H * ((W + 127) / 128) * 2;
+}
+
+template <int K, int SEG, int NCP>
+static hipError_t launch_dy_bf16(dim3 grid, const void *x, const void *wg, const void *gout, void *gy, int H, int W,
+                                 hipStream_t stream) {
+    using P = DyPlanB<K, SEG, NCP>;
+    constexpr int lds = P::LDS;
+    auto kern = bwd_dy_bf16_kernel<K, SEG, NCP>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(P::THREADS), lds, stream, (const bf16_t *)x, (const bf16_t *)wg,
+                       (const bf16_t *)gout, (bf16_t *)gy, H, W);
+    return hipGetLastError();
 }
 
 template <int K>
-static hipError_t launch_dy_bf16(dim3 grid, const void *x, const void *wg, const void *gout, void *gy, int H, int W,
-                                 hipStream_t stream) {
-    constexpr int lds = DyPlanB<K>::LDS;
-    auto kern = bwd_dy_bf16_kernel<K>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(kThreadsB), lds, stream, (const bf16_t *)x, (const bf16_t *)wg, (const bf16_t *)gout,
-                       (bf16_t *)gy, H, W);
-    return hipGetLastError();
+static hipError_t launch_dy_bf16_k(dim3 grid, bool wide, const void *x, const void *wg, const void *gout, void *gy,
+                                   int H, int W, hipStream_t stream) {
+    if (wide) return launch_dy_bf16<K, 256, 64>(grid, x, wg, gout, gy, H, W, stream);
+    return launch_dy_bf16<K, 128, 32>(grid, x, wg, gout, gy, H, W, stream);
 }
 
 hipError_t launch_bwd_dy_rows(const void *x, const void *wg, const void *gout, void *gy, int N, int H, int W, int K,
@@ -523,10 +554,11 @@ hipError_t launch_bwd_dy_rows(const void *x, const void *wg, const void *gout, v
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nblk), block(256);
     if (bf16) {
+        const bool wide = dy_bf16_wide(N, H, W);
         switch (K) {
-            case 1: return launch_dy_bf16<1>(grid, x, wg, gout, gy, H, W, stream);
-            case 3: return launch_dy_bf16<3>(grid, x, wg, gout, gy, H, W, stream);
-            default: return launch_dy_bf16<5>(grid, x, wg, gout, gy, H, W, stream);
+            case 1: return launch_dy_bf16_k<1>(grid, wide, x, wg, gout, gy, H, W, stream);
+            case 3: return launch_dy_bf16_k<3>(grid, wide, x, wg, gout, gy, H, W, stream);
+            default: return launch_dy_bf16_k<5>(grid, wide, x, wg, gout, gy, H, W, stream);
         }
     }
     const float *X = (const float *)x, *Wg = (const float *)wg, *G = (const float *)gout;
