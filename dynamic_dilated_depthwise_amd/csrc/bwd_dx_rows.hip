@@ -210,6 +210,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
     if (NST > 1) load_stage(1);
     __syncthreads();
 
+    // A block's product with G_b is applied after the next block's MFMAs (across tap
+    // and stage boundaries: it only touches registers), so the MFMA result is not
+    // waited for right away.  pacc / pgf / ppb: the pending block, pend: whether
+    // there is one (its tap read a row inside the image).
+    f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+    u16x4 pgraw = {0, 0, 0, 0};
+    bool pend = false;
+    auto retire = [&](int ppb) {
+        float gf[4];
+        widen4(pgraw, gf);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dacc[ppb][v] += round_to_bf16(pacc[v]) * gf[v];
+    };
+
 #pragma clang loop unroll(full)
     for (int st = 0; st < NST; ++st) {
         const int b = st / K;
@@ -237,11 +251,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
                     const u16x4 graw = *(const u16x4_a2 *)(gb + pb * 32);
                     f32x4 acc = mfma_16x16x32_bf16(a0, cur.b0, bias4);
                     acc = mfma_16x16x32_bf16(a1, cur.b1, acc);
-                    float gf[4];
-                    widen4(graw, gf);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) dacc[pb][v] += round_to_bf16(acc[v]) * gf[v];
+                    if (pend) retire(pb == 0 ? 3 : pb - 1);
+                    pacc = acc;
+                    pgraw = graw;
+                    pend = true;
                 }
+            } else if (pend) {
+                retire(3);
+                pend = false;
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -251,6 +268,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
             if (st + 2 < NST) load_stage(st + 2);
         }
     }
+
+    if (pend) retire(3);
 
     // dX = G_x + the gathered sum, rounded once
     const bf16_t *gxr = gn + c * HW + h * W + w0 + 4 * g;
