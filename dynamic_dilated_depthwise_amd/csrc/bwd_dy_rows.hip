@@ -12,8 +12,10 @@
 // (wave v takes c = 16v .. 16v+15, four k-steps of 4) and every wave walks the same
 // (branch, kernel row) stages, so one staging serves them all: per stage the x row
 // h + dr (dr = (ki - r) * D_b, with a column halo) and, when the branch changes,
-// the G_b row h are copied into LDS as channel rows, once, between two barriers;
-// their global loads are issued a whole stage ahead.  Each tap is 64 MFMAs
+// the G_b row h are copied into LDS as channel rows, once; x is double-buffered by
+// stage and G_b by branch, so the copy of the next stage follows the current
+// stage's products with one barrier per stage, and its global loads are issued two
+// stages ahead.  Each tap is 64 MFMAs
 // (v_mfma_f32_16x16x4_f32) per wave:
 //   rows    = 16 output channels of block mb: row i is channel 4i + mb, so a lane's
 //             four weights of one generator row are one 16-byte load;
@@ -59,7 +61,9 @@ template <int K> struct DyPlan {
     static constexpr int XBUF = kChY * XROW;
     static constexpr int GBUF = kChY * GROW;
     static constexpr int RED = 4 * 64 * 32;           // floats: the partials of two output blocks of four waves
-    static constexpr int LDS = (XBUF + GBUF) > RED ? (XBUF + GBUF) : RED;
+    // two x buffers (stage parity) and two G_b buffers (branch parity): the copy of
+    // the next stage goes to the buffers the current stage does not read
+    static constexpr int LDS = 2 * (XBUF + GBUF) > RED ? 2 * (XBUF + GBUF) : RED;
 };
 
 template <int K>
@@ -74,8 +78,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
     constexpr int NST = P::NST;
     constexpr int C = kChY;
     __shared__ __align__(16) float lds[P::LDS];
-    float *xs = lds;             // staged x row   [c][XROW]
-    float *gsb = lds + P::XBUF;  // staged G_b row [c][GROW]
+    // staged x rows [2][c][XROW] by stage parity, G_b rows [2][c][GROW] by branch parity
+    float *xs0 = lds;
+    float *gs0 = lds + 2 * P::XBUF;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -146,6 +151,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
     };
     auto store_stage = [&](int st) {
         const int hs = x_row(st);
+        float *xs = xs0 + (st & 1) * P::XBUF;
+        float *gsb = gs0 + ((st / K) & 1) * P::GBUF;
         if (hs >= 0 && hs < H) {
 #pragma unroll
             for (int k = 0; k < XIT; ++k)
@@ -176,11 +183,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
         for (int pb = 0; pb < 4; ++pb) acc[mb][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     WOps ring[2];  // operands of tap bt in ring[bt & 1]
-    load_stage(0);
-    fetch(0, ring[0]);
     // lane's x / G runs: channel 16v + 4s + g, pixels 4j .. 4j+3 (x shifted by dc)
     const int x_lane = (16 * wave + g) * P::XROW + 4 * j;
     const int g_lane = (16 * wave + g) * P::GROW + 4 * j;
+    // stage 0 is copied before the loop; the copy of stage st+1 follows stage st's
+    // products, into the other buffers, and one barrier per stage separates them
+    load_stage(0);
+    fetch(0, ring[0]);
+    store_stage(0);
+    __syncthreads();
+    if (NST > 1) load_stage(1);
 #pragma clang loop unroll(full)
     for (int st = 0; st < NST; ++st) {
         const int b = st / K;
@@ -188,10 +200,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
         const int D = 1 + 2 * b;
         const int hs = h + (ki - r) * D;
         const bool rok = hs >= 0 && hs < H;
-        if (st > 0) __syncthreads();  // every wave is done reading the previous stage
-        store_stage(st);
-        __syncthreads();
-        if (st + 1 < NST) load_stage(st + 1);
+        const float *xs = xs0 + (st & 1) * P::XBUF;
+        const float *gsb = gs0 + (b & 1) * P::GBUF;
 #pragma clang loop unroll(full)
         for (int kj = 0; kj < K; ++kj) {
             const int bt = b * KK + ki * K + kj;
@@ -216,6 +226,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
                 __builtin_amdgcn_s_setprio(0);
             }
         }
+        if (st + 1 < NST) store_stage(st + 1);
+        __syncthreads();
+        if (st + 2 < NST) load_stage(st + 2);
     }
 
     // ---- the four waves' partial sums, added in wave order: two output blocks at a
