@@ -64,3 +64,16 @@ def test_bench_module_cli():
     r = subprocess.run([_sys.executable, "-m", "dynamic_dilated_depthwise_amd.bench_module", "--help"],
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 0 and "--memory-child" in r.stdout
+
+
+def test_cpu_baseline_sample_stops_after_its_floor():
+    """The oracle baseline times at least three steps after one warm-up, keeps going
+    until its time floor is met, and never passes its step cap."""
+    shape = synth.Shape(1, 4, 8, 8, 3)
+    h = synth.make_inputs(shape, 1, taps=True, grad=True)
+    t = bench.run_cpu_baseline(h, shape, min_reps=3, min_s=0.0, max_reps=5)
+    assert t["reps"] == 3
+    t = bench.run_cpu_baseline(h, shape, min_reps=3, min_s=1e9, max_reps=5)
+    assert t["reps"] == 5 and t["timed_s"] > 0
+    for k in ("filter", "fused_fwd", "fused_bwd"):
+        assert t[k] > 0
