@@ -472,7 +472,7 @@ hipError_t launch_dx_t(const void *y, const void *wg, const void *bg, const void
     };
     // row-staged kernel from one 64-pixel segment per CU up (measured at 128x128,
     // C = 64: K = 5 bf16 140 -> 55 us, fp32 146 -> 108 us; K = 3 bf16 60 -> 28 us)
-    if (nblk >= kCUs && bwd_dx_rows_applies(C, H, W, al))
+    if (nblk >= kCUs && bwd_dx_rows_applies(C, H, W, al, Elem<T>::is_bf16))
         return launch_bwd_dx_rows(y, wg, bg, gout, gx, N, H, W, K, Elem<T>::is_bf16, stream);
     if (nblk <= kCUs) {
         if (fullw) launch(bwd_dx_kernel<T, K, 4, !Elem<T>::is_bf16>, 1024);

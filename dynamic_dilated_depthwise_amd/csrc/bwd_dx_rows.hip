@@ -22,10 +22,15 @@
 // segment with a column halo, all 64 channels, in LDS as eight planes of 8
 // channels ([c/8][pixel][c%8], 16 bytes per pixel), so any column shift is an
 // immediate offset and the 16 lanes of a fragment read 256 contiguous bytes.
-// Stages (7 at K = 3, 13 at K = 5, 1 at K = 1) are double-buffered with one barrier
-// each; a stage whose source row lies outside the image contributes nothing and is
-// skipped.  Every tap is unrolled at compile time, so no index arithmetic runs per
-// tap.  The sum over taps runs in stage order (float32), then G_x is added.
+// bfloat16 stages are the 3K (branch, kernel row) pairs, y and G_b together,
+// double-buffered with one barrier each and loaded two stages ahead with buffer
+// loads (fixed per-thread offsets, the row as a scalar offset, zero outside the
+// image); G_b is read back as aligned dwords, since 2-byte-aligned 8-byte LDS
+// reads cost the kernel a sixth of its time.  A stage whose source row lies
+// outside the image contributes nothing and is skipped.  Every tap is unrolled at
+// compile time, so no index arithmetic runs per tap.  The sum over taps runs in
+// stage order in float32 (bfloat16: pairs of taps through the two-term dot
+// instruction), then G_x is added.
 #include "common.hpp"
 #include "launchers.hpp"
 
@@ -58,8 +63,8 @@ template <int K> struct DxStageBuf {
     unsigned char g[DxPlan<K>::GBUF];
 };
 
-typedef uint16_t u16x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Widen a run of four bf16 values (two dwords) to float.
 __device__ __forceinline__ void widen4(const u16x4 u, float (&f)[4]) {
@@ -69,6 +74,16 @@ __device__ __forceinline__ void widen4(const u16x4 u, float (&f)[4]) {
     f[2] = __uint_as_float(d[1] << 16);
     f[3] = __uint_as_float(d[1] & 0xffff0000u);
 }
+
+// Two floats rounded to bfloat16 (nearest even) in one dword: lo, hi.
+__device__ __forceinline__ bf16x2_t rne_pair(float lo, float hi) { return bf16x2_t{(__bf16)lo, (__bf16)hi}; }
+
+// Buffer resource over `bytes` bytes at p (gfx9 word 3: raw 32-bit data).  A load
+// whose offset lies past the end reads zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+constexpr unsigned kOob = 0x7ffffff0u;  // a buffer offset that always reads zero
 
 template <int K>
 __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__restrict__ y,
@@ -100,17 +115,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
     const bf16_t *__restrict__ gn = gout + (int64_t)n * 4 * C * HW;
     const int c = 16 * wave + i;  // the output channel of this lane's MFMA column
 
-    // ---- staging.  y: thread tid covers blocks of 4 channels x 4 pixels (transposed
-    // into the planes); G_b: runs of 4 pixels of one channel row (copied as they are).
+    // ---- staging through buffer loads: every per-thread offset is fixed, the
+    // stage's row is a scalar offset, and a run outside the image reads zero (no
+    // branches, no 64-bit address arithmetic).  y: thread tid covers blocks of 4
+    // channels x 4 pixels (transposed into the planes); G_b: runs of 4 pixels of one
+    // channel row (copied as they are).
+    const __amdgpu_buffer_rsrc_t ry = buf_rsrc(yn, C * HW * 2);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gn, 4 * C * HW * 2);
     constexpr int NB4 = P::SW / 4;            // 4-pixel runs per staged row
     constexpr int NBLK = 16 * NB4;            // y blocks
     constexpr int YIT = (NBLK + 255) / 256;   // y blocks per thread
     constexpr int NRUN = kChX * NB4;          // G runs
     constexpr int GIT = (NRUN + 255) / 256;   // G runs per thread
-    u16x4 yreg[YIT][4];
-    u16x4 greg[GIT];
-    int yoff[YIT], ydst[YIT], goff[GIT], gdst[GIT];
-    bool yok[YIT], yex[YIT], gok[GIT], gex[GIT];
+    u32x2_t yreg[YIT][4];
+    u32x2_t greg[GIT];
+    unsigned yvo[YIT][4], gvo[GIT];  // byte offsets within the stage's row, or kOob
+    int ydst[YIT], gdst[GIT];
+    bool yex[YIT], gex[GIT];
 #pragma unroll
     for (int k = 0; k < YIT; ++k) {
         const int q = tid + 256 * k;
@@ -118,8 +139,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
         const int px4 = q - c4 * NB4;
         const int col = w0 - P::LP + 4 * px4;
         yex[k] = q < NBLK;
-        yok[k] = yex[k] && col >= 0 && col < W;  // W % 4 == 0: a run is wholly in or out
-        yoff[k] = 4 * c4 * HW + col;
+        const bool ok = yex[k] && col >= 0 && col < W;  // W % 4 == 0: a run is wholly in or out
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yvo[k][e] = ok ? (unsigned)((4 * c4 + e) * HW + col) * 2u : kOob;
         ydst[k] = (c4 >> 1) * P::PLANE + 4 * px4 * 16 + (c4 & 1) * 8;
     }
 #pragma unroll
@@ -129,8 +151,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
         const int px4 = q - ch * NB4;
         const int col = w0 - P::LP + 4 * px4;
         gex[k] = q < NRUN;
-        gok[k] = gex[k] && col >= 0 && col < W;
-        goff[k] = ch * HW + col;
+        const bool ok = gex[k] && col >= 0 && col < W;
+        gvo[k] = ok ? (unsigned)(ch * HW + col) * 2u : kOob;
         gdst[k] = (ch * P::GROW + 4 * px4) * 2;
     }
     // global loads of stage st (branch b = st / K, kernel row ki = st % K) into registers
@@ -139,22 +161,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
         const int ki = st - b * K;
         const int hs = h - (ki - r) * (1 + 2 * b);
         if (hs < 0 || hs >= H) return;  // wave-uniform: the stage is skipped
-        const bf16_t *ybase = yn + hs * W;
-        const bf16_t *gbase = gn + (1 + b) * C * HW + hs * W;
+        const int yso = hs * W * 2;
+        const int gso = ((1 + b) * C * HW + hs * W) * 2;
 #pragma unroll
         for (int k = 0; k < YIT; ++k)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u16x4 v = {0, 0, 0, 0};
-                if (yok[k]) v = *(const u16x4 *)(ybase + yoff[k] + e * HW);
-                yreg[k][e] = v;
-            }
+            for (int e = 0; e < 4; ++e) yreg[k][e] = __builtin_amdgcn_raw_buffer_load_b64(ry, yvo[k][e], yso, 0);
 #pragma unroll
-        for (int k = 0; k < GIT; ++k) {
-            u16x4 v = {0, 0, 0, 0};
-            if (gok[k]) v = *(const u16x4 *)(gbase + goff[k]);
-            greg[k] = v;
-        }
+        for (int k = 0; k < GIT; ++k) greg[k] = __builtin_amdgcn_raw_buffer_load_b64(rg, gvo[k], gso, 0);
     };
     auto store_stage = [&](int st, int buf) {
         const int b = st / K;
@@ -168,29 +182,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 u16x4 o;
-                o[0] = yreg[k][0][p]; o[1] = yreg[k][1][p]; o[2] = yreg[k][2][p]; o[3] = yreg[k][3][p];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(u16x4, yreg[k][e])[p];
                 *(u16x4 *)(d + 16 * p) = o;
             }
         }
 #pragma unroll
         for (int k = 0; k < GIT; ++k)
-            if (gex[k]) *(u16x4 *)(sb[buf].g + gdst[k]) = greg[k];
+            if (gex[k]) *(u32x2_t *)(sb[buf].g + gdst[k]) = greg[k];
     };
 
-    // ---- the tap loop.  Weight fragments of tap (b, t): row o = (b*C + c)*KK + t,
-    // columns 32 sub + 8g .. +7, and the row's bias; fetched two taps ahead (a ring
-    // of three).
-    const bf16_t *__restrict__ wl = wg + c * KK * C + 8 * g;
-    const bf16_t *__restrict__ bgl = bg + c * KK;
-    struct WOps { bf16x8 b0, b1; bf16_t bias; };
-    WOps wring[3];
+    // ---- weight fragments of tap (b, t): row o = (b*C + c)*KK + t, columns 32 sub +
+    // 8g .. +7, and the row's bias, by buffer loads whose tap part is a constant
+    // offset.  A ring of four: the taps of the current pair and of the next.
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wg, 3 * C * KK * C * 2);
+    const __amdgpu_buffer_rsrc_t rb = buf_rsrc(bg, 3 * C * KK * 2);
+    const unsigned wvo = (unsigned)(c * KK * C + 8 * g) * 2u;
+    const unsigned bvo = (unsigned)(c * KK) * 2u;
+    struct WOps { bf16x8 b0, b1; uint16_t bias; };
+    WOps wring[4];
     auto fetch_w = [&](int bt, WOps &o) {  // bt = b*KK + t
         const int b = bt / KK;
         const int t = bt - b * KK;
-        const bf16_t *wt = wl + (b * C * KK + t) * C;
-        o.b0 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(wt));
-        o.b1 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(wt + 32));
-        o.bias = bgl[b * C * KK + t];
+        const int wso = (b * C * KK + t) * C * 2;
+        o.b0 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo, wso, 0));
+        o.b1 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo, wso + 64, 0));
+        o.bias = __builtin_amdgcn_raw_buffer_load_b16(rb, bvo, (b * C * KK + t) * 2, 0);
     };
     // A fragment (y): plane 4*sub + g, pixel 16pb + i + (LP - dc)
     const int a_lane = g * P::PLANE + i * 16;
@@ -210,20 +227,61 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
     if (NST > 1) load_stage(1);
     __syncthreads();
 
-    // A block's product with G_b is applied after the next block's MFMAs (across tap
-    // and stage boundaries: it only touches registers), so the MFMA result is not
-    // waited for right away.  pacc / pgf / ppb: the pending block, pend: whether
-    // there is one (its tap read a row inside the image).
-    f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
-    u16x4 pgraw = {0, 0, 0, 0};
+    // The K taps of a stage run as pairs (kj, kj + 1) and, for odd K, a last single
+    // tap.  A pair's two rounded taps meet G_b at their two source pixels in one
+    // two-term bf16 dot product with float32 accumulation (v_dot2_f32_bf16), which
+    // sums the pair's two exact products into the running sum.  An item (a pair or
+    // single, one pixel block) is applied after the next item's MFMAs, across stage
+    // boundaries too (it only touches registers), so its MFMA results are not waited
+    // for right away.  pacc / pg: the pending item, pend: whether there is one.
+    constexpr int NPAIR = K / 2;
+    constexpr int NGRP = (K + 1) / 2;
+    f32x4 pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // G_b runs are read from LDS as aligned dwords: the run of a tap whose column
+    // shift is odd starts in the high half of its first dword and spans three.  A
+    // group's first tap (and a single tap) has shift parity r & 1, its second the
+    // other, whatever the branch, so the position of each value is a constant.
+    constexpr int PAR0 = r & 1;
+    uint32_t pg[2][3] = {{0u, 0u, 0u}, {0u, 0u, 0u}};
     bool pend = false;
-    auto retire = [&](int ppb) {
-        float gf[4];
-        widen4(pgraw, gf);
+    auto retire = [&](bool pair, int ppb) {
+        if (pair) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dacc[ppb][v] += round_to_bf16(pacc[v]) * gf[v];
+            for (int v = 0; v < 4; ++v) {
+                const bf16x2_t q = rne_pair(pacc[0][v], pacc[1][v]);
+                // lo half: value v of the first tap's run, hi half: of the second's
+                const int p0 = PAR0 + v, p1 = 1 - PAR0 + v;
+                const uint32_t sel = (p0 & 1 ? 0x0302u : 0x0100u) | (p1 & 1 ? 0x07060000u : 0x05040000u);
+                const uint32_t gw = __builtin_amdgcn_perm(pg[1][p1 >> 1], pg[0][p0 >> 1], sel);
+                dacc[ppb][v] = __builtin_amdgcn_fdot2_f32_bf16(q, __builtin_bit_cast(bf16x2_t, gw), dacc[ppb][v], false);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; v += 2) {
+                const uint32_t q = __builtin_bit_cast(uint32_t, rne_pair(pacc[0][v], pacc[0][v + 1]));
+                const int pa = PAR0 + v, pbb = PAR0 + v + 1;
+                const float ga = __uint_as_float(pa & 1 ? pg[0][pa >> 1] & 0xffff0000u : pg[0][pa >> 1] << 16);
+                const float gb = __uint_as_float(pbb & 1 ? pg[0][pbb >> 1] & 0xffff0000u : pg[0][pbb >> 1] << 16);
+                dacc[ppb][v] += __uint_as_float(q << 16) * ga;
+                dacc[ppb][v + 1] += __uint_as_float(q & 0xffff0000u) * gb;
+            }
+        }
     };
 
+    // LDS operands of one item (group gi, pixel block pb): per tap, the two A
+    // fragments and the G_b run.
+    struct Ops {
+        bf16x8 a0[2], a1[2];
+        uint32_t g[2][3];
+    };
+    int fetched = NT > 1 ? 2 : 1;  // taps whose weights are requested (compile-time after unrolling)
+    // request the weights up to two taps past group gi of stage st (ring slot = tap
+    // % 4; the slot's previous tap belongs to an earlier group)
+    auto fetch_upto = [&](int st, int gi) {
+        const int bt0 = st * K + 2 * gi;
+        const int nt = gi < NPAIR ? 2 : 1;
+        for (; fetched < NT && fetched < bt0 + nt + 2; ++fetched) fetch_w(fetched, wring[fetched & 3]);
+    };
 #pragma clang loop unroll(full)
     for (int st = 0; st < NST; ++st) {
         const int b = st / K;
@@ -231,36 +289,75 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
         const int D = 1 + 2 * b;
         const int hs = h - (ki - r) * D;
         const bool rok = hs >= 0 && hs < H;  // wave-uniform: taps reading outside the image add nothing
-        const unsigned char *ybuf = sb[st & 1].y;
-        const unsigned char *gbuf = sb[st & 1].g;
-#pragma clang loop unroll(full)
-        for (int kj = 0; kj < K; ++kj) {
-            const int bt = b * KK + ki * K + kj;  // this tap; taps run in (b, t) order
-            const WOps cur = wring[bt % 3];
-            if (bt + 2 < NT) fetch_w(bt + 2, wring[(bt + 2) % 3]);
-            if (rok) {
-                const int dc = (kj - r) * D;
-                const float bias = bf16_bits_to_f32(cur.bias);
-                const f32x4 bias4 = {bias, bias, bias, bias};
-                const unsigned char *ab = ybuf + a_lane + (P::LP - dc) * 16;
-                const unsigned char *gb = gbuf + g_lane + (P::LP - dc) * 2;
+        const unsigned char *ybuf = sb[st & 1].y + a_lane;
+        const unsigned char *gbuf = sb[st & 1].g + g_lane;
+        auto load_ops = [&](int gi, int pb, Ops &o) {
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb) {
-                    const bf16x8 a0 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(ab + pb * 256));
-                    const bf16x8 a1 = __builtin_bit_cast(bf16x8, *(const u16x8 *)(ab + pb * 256 + 4 * P::PLANE));
-                    const u16x4 graw = *(const u16x4_a2 *)(gb + pb * 32);
-                    f32x4 acc = mfma_16x16x32_bf16(a0, cur.b0, bias4);
-                    acc = mfma_16x16x32_bf16(a1, cur.b1, acc);
-                    if (pend) retire(pb == 0 ? 3 : pb - 1);
-                    pacc = acc;
-                    pgraw = graw;
-                    pend = true;
+            for (int u = 0; u < 2; ++u) {
+                if (u >= (gi < NPAIR ? 2 : 1)) continue;
+                const int dc = (2 * gi + u - r) * D;
+                const unsigned char *ab = ybuf + (P::LP - dc) * 16 + pb * 256;
+                o.a0[u] = __builtin_bit_cast(bf16x8, *(const u16x8 *)ab);
+                o.a1[u] = __builtin_bit_cast(bf16x8, *(const u16x8 *)(ab + 4 * P::PLANE));
+                const int par = u == 0 ? PAR0 : 1 - PAR0;  // == (LP - dc) & 1
+                const uint32_t *gw = (const uint32_t *)(gbuf + (P::LP - dc - par) * 2 + pb * 32);
+#pragma unroll
+                for (int m = 0; m < 3; ++m) o.g[u][m] = m < 2 + par ? gw[m] : 0u;
+            }
+        };
+        if (rok) {
+            constexpr int NIT = 4 * NGRP;  // items of the stage: (group, pixel block)
+            f32x4 bias4[2];
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int gi = it / 4;
+                const int pb = it % 4;
+                const bool pair = gi < NPAIR;
+                const int nt = pair ? 2 : 1;
+                const int bt0 = st * K + 2 * gi;  // first tap of the group; taps run in (b, t) order
+                if (pb == 0) {
+                    fetch_upto(st, gi);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const float bias = bf16_bits_to_f32(wring[(bt0 + u) & 3].bias);
+                        if (u < nt) bias4[u] = f32x4{bias, bias, bias, bias};
+                    }
                 }
-            } else if (pend) {
-                retire(3);
+                Ops o;
+                load_ops(gi, pb, o);
+                f32x4 acc[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (u >= nt) continue;
+                    const WOps &cur = wring[(bt0 + u) & 3];
+                    acc[u] = mfma_16x16x32_bf16(o.a0[u], cur.b0, bias4[u]);
+                    acc[u] = mfma_16x16x32_bf16(o.a1[u], cur.b1, acc[u]);
+                }
+                // the pending item: the previous one of this stage, else the last
+                // item (pixel block 3 of the last group) of an earlier stage
+                if (pend) {
+                    if (pb > 0) retire(pair, pb - 1);
+                    else if (gi > 0) retire(gi - 1 < NPAIR, 3);
+                    else retire(NGRP - 1 < NPAIR, 3);
+                }
+                pacc[0] = acc[0];
+#pragma unroll
+                for (int m = 0; m < 3; ++m) pg[0][m] = o.g[0][m];
+                if (pair) {
+                    pacc[1] = acc[1];
+#pragma unroll
+                    for (int m = 0; m < 3; ++m) pg[1][m] = o.g[1][m];
+                }
+                pend = true;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int gi = 0; gi < NGRP; ++gi) fetch_upto(st, gi);
+            if (pend) {  // the pending item is the last of an earlier stage
+                retire(NGRP - 1 < NPAIR, 3);
                 pend = false;
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         if (st + 1 < NST) {
             store_stage(st + 1, (st + 1) & 1);
@@ -269,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
         }
     }
 
-    if (pend) retire(3);
+    if (pend) retire(NGRP - 1 < NPAIR, 3);
 
     // dX = G_x + the gathered sum, rounded once
     const bf16_t *gxr = gn + c * HW + h * W + w0 + 4 * g;
@@ -526,9 +623,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
 }  // namespace
 
 // Applicability: C = 64, W % 4 == 0, 16-byte aligned tensors (checked by the
-// caller) and plane offsets within 32 bits.
-bool bwd_dx_rows_applies(int C, int H, int W, bool al) {
-    return C == kChX && al && (W % 4) == 0 && (int64_t)4 * kChX * H * W < (int64_t(1) << 31);
+// caller) and the 4C gradient planes of an image within 32-bit offsets (float32:
+// element offsets; bfloat16: the buffer loads' byte offsets).
+bool bwd_dx_rows_applies(int C, int H, int W, bool al, bool bf16) {
+    return C == kChX && al && (W % 4) == 0 && (int64_t)4 * kChX * H * W * (bf16 ? 2 : 1) < (int64_t(1) << 31);
 }
 
 hipError_t launch_bwd_dx_rows(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,

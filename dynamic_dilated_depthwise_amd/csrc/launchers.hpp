@@ -27,7 +27,7 @@ hipError_t launch_bwd_dx(const void *y, const void *wg, const void *bg, const vo
 
 // dX for C = 64 staged by source row (both dtypes); bwd_dx_rows_applies tells
 // whether a shape can take it.
-bool bwd_dx_rows_applies(int C, int H, int W, bool al);
+bool bwd_dx_rows_applies(int C, int H, int W, bool al, bool bf16);
 hipError_t launch_bwd_dx_rows(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
                               int H, int W, int K, bool bf16, hipStream_t stream);
 
