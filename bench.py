@@ -247,6 +247,28 @@ def measure(args, ddpm, synth, dt_name, log_prefix=""):
            for i, (name, _) in enumerate(calls)}
     log(f"{log_prefix}per-call ms " + " ".join(f"{k}={v:.4f}" for k, v in per.items()))
 
+    # The fused training sequence as a module runs it: the forward, one backward call
+    # that launches dX, dY and the dW partials back to back, and the reduction, with
+    # one event pair per sequence (the per-call events above add a marker of about
+    # 5 us to every kernel they bracket).
+    def train_seq():
+        ddpm.ddpm_fused_fwd(d["x"], d["y"], d["weight"], d["bias"], out, K, stream)
+        ddpm.ddpm_fused_bwd(d["x"], d["y"], d["weight"], d["bias"], d["grad_out"], gx, gy, pw, pb, K, stream)
+        ddpm.ddpm_reduce_partials(pw, pb, gw, gb, K, stream)
+
+    for _ in range(args.warmup):
+        train_seq()
+    sev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in sev:
+        e0.record(stream)
+        train_seq()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    seq_ts = sorted(e0.elapsed_time(e1) for e0, e1 in sev)
+    train_seq_ms = seq_ts[len(seq_ts) // 2]
+    log(f"{log_prefix}fused fwd+bwd sequence (one event pair) median ms={train_seq_ms:.4f}")
+
     for name, fn in extra_calls:
         for _ in range(args.warmup):
             fn()
@@ -331,7 +353,8 @@ def measure(args, ddpm, synth, dt_name, log_prefix=""):
     res = {
         "dtype": dt_name, "shape": shape, "S": S, "h": h, "alg": alg, "ms_per_step": ms_per_step,
         "value_timing": value_timing, "filter_tbs": filter_tbs, "filter_warm_tbs": filter_warm_tbs,
-        "filter_ms": per["filter"], "fwd_ms": fwd_ms, "fwd_bwd_ms": fwd_bwd_ms, "gen_tflops": gen_tflops,
+        "filter_ms": per["filter"], "fwd_ms": fwd_ms, "fwd_bwd_ms": fwd_bwd_ms, "train_seq_ms": train_seq_ms,
+        "gen_tflops": gen_tflops,
         "peak_t": peak_t, "kernels": kernels, "roofline": roofline,
     }
     del d, out_f, out, gx, gy, pw, pb, gw, gb, gx_f, gk_f
@@ -351,6 +374,7 @@ def summary(m):
         "filter_warm_hbm_frac": m["kernels"]["filter"]["frac"],
         "fused_fwd_ms": round(m["fwd_ms"], 5),
         "fused_fwd_bwd_ms": round(m["fwd_bwd_ms"], 5),
+        "fused_fwd_bwd_seq_ms": round(m["train_seq_ms"], 5),
         "fused_fwd_mfma_tflops": round(m["gen_tflops"], 2),
         "fused_fwd_mfma_frac": round(m["gen_tflops"] / m["peak_t"], 4),
         "kernels": m["kernels"],
