@@ -256,14 +256,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
                 dacc[ppb][v] = __builtin_amdgcn_fdot2_f32_bf16(q, __builtin_bit_cast(bf16x2_t, gw), dacc[ppb][v], false);
             }
         } else {
+            // a single tap: the same dot instruction with a zero second term (the
+            // rounded tap and its G_b value in the low halves, exact zeros above)
 #pragma unroll
-            for (int v = 0; v < 4; v += 2) {
-                const uint32_t q = __builtin_bit_cast(uint32_t, rne_pair(pacc[0][v], pacc[0][v + 1]));
-                const int pa = PAR0 + v, pbb = PAR0 + v + 1;
-                const float ga = __uint_as_float(pa & 1 ? pg[0][pa >> 1] & 0xffff0000u : pg[0][pa >> 1] << 16);
-                const float gb = __uint_as_float(pbb & 1 ? pg[0][pbb >> 1] & 0xffff0000u : pg[0][pbb >> 1] << 16);
-                dacc[ppb][v] += __uint_as_float(q << 16) * ga;
-                dacc[ppb][v + 1] += __uint_as_float(q & 0xffff0000u) * gb;
+            for (int v = 0; v < 4; ++v) {
+                const bf16x2_t q = rne_pair(pacc[0][v], 0.f);
+                const int p0 = PAR0 + v;
+                const uint32_t gw = p0 & 1 ? pg[0][p0 >> 1] >> 16 : pg[0][p0 >> 1] & 0xffffu;
+                dacc[ppb][v] = __builtin_amdgcn_fdot2_f32_bf16(q, __builtin_bit_cast(bf16x2_t, gw), dacc[ppb][v], false);
             }
         }
     };
