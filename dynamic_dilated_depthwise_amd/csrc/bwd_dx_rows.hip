@@ -64,7 +64,6 @@ template <int K> struct DxStageBuf {
 };
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Widen a run of four bf16 values (two dwords) to float.
 __device__ __forceinline__ void widen4(const u16x4 u, float (&f)[4]) {

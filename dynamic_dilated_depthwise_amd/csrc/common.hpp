@@ -13,6 +13,7 @@ namespace ddpm {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 

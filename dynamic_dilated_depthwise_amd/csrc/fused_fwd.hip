@@ -17,6 +17,7 @@
 // y is read once per wave into registers (the MFMA B operand is the same for
 // all 3*K*K generator blocks) when C <= 64; larger C streams it per block.
 #include <algorithm>
+#include <type_traits>
 
 #include "gen_mma.hpp"
 #include "launchers.hpp"
@@ -256,6 +257,98 @@ __global__ __launch_bounds__(GRP3 ? 768 : 256, GRP3 ? 3 : 2) void fused_fwd_kern
 #pragma unroll
             for (int q = 0; q < (KQ > 0 ? KQ : 1); ++q) af[q] = G::load_A(arow, q, g, C, cvec);
         };
+        if constexpr (Elem<T>::is_bf16 && KQ > 0) {
+            // bfloat16: taps in pairs (t, t+1).  The pair's two rounded taps of one
+            // channel and pixel share a packed dword (v_cvt_pk_bf16_f32), their x
+            // values another (the high halves of the staged floats, which are the
+            // bf16 inputs exactly; v_perm_b32), and v_dot2_f32_bf16 adds both exact
+            // products to the float32 sum.  An odd last tap pairs with zeros.  The
+            // weights of the next pair are fetched into the fragments of this one once
+            // its MFMAs are issued; the biases and x values are read before the MFMAs.
+            // FULL (wave-uniform) is tested once, outside the loop.
+            auto run_pairs = [&](auto fullc) {
+                constexpr bool FULL = decltype(fullc)::value;
+                auto fetch2 = [&](int t, typename G::AFrag (&af)[KQ]) {
+                    if constexpr (FULL) {
+                        const T *wbt = wg + ((int64_t)b * C * KK + t) * C;
+#pragma unroll
+                        for (int q = 0; q < KQ; ++q) af[q] = G::load_A_off(wbt, aoff + G::CH * q);
+                    } else {
+                        const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
+#pragma unroll
+                        for (int q = 0; q < KQ; ++q) af[q] = G::load_A(arow, q, g, C, cvec);
+                    }
+                };
+                auto read_x = [&](int t, float (&xv)[4][4]) {
+                    const int ki = t / K;
+                    const int kj = t - ki * K;
+                    const float *xl = xs + (wave + X::HALO + (ki - r) * D) * X::LW + 4 * j + X::PADC + (kj - r) * D;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) xv[v][pb] = xl[(4 * g + v) * X::PLANE + pb];
+                };
+                typename G::AFrag wa0[KQ], wa1[KQ];
+                fetch2(0, wa0);
+                if (KK > 1) fetch2(1, wa1);
+                int t = 0;
+#pragma unroll 1
+                for (; t + 1 < KK; t += 2) {
+                    const f32x4 bias0 = *(const f32x4 *)(bl + (b * KK + t) * 16 + 4 * g);
+                    const f32x4 bias1 = *(const f32x4 *)(bl + (b * KK + t + 1) * 16 + 4 * g);
+                    float x0[4][4], x1[4][4];
+                    read_x(t, x0);
+                    read_x(t + 1, x1);
+                    f32x4 acc0[4], acc1[4];
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) {
+                        acc0[pb] = bias0;
+                        acc1[pb] = bias1;
+                    }
+#pragma unroll
+                    for (int q = 0; q < KQ; ++q) G::mma(acc0, wa0[q], bres[q]);
+#pragma unroll
+                    for (int q = 0; q < KQ; ++q) G::mma(acc1, wa1[q], bres[q]);
+                    if (t + 2 < KK) fetch2(t + 2, wa0);
+                    if (t + 3 < KK) fetch2(t + 3, wa1);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) {
+                            const bf16x2_t qp = bf16x2_t{(__bf16)acc0[pb][v], (__bf16)acc1[pb][v]};
+                            const uint32_t xp = __builtin_amdgcn_perm(__float_as_uint(x1[v][pb]),
+                                                                      __float_as_uint(x0[v][pb]), 0x07060302u);
+                            oacc[b][v][pb] = __builtin_amdgcn_fdot2_f32_bf16(qp, __builtin_bit_cast(bf16x2_t, xp),
+                                                                             oacc[b][v][pb], false);
+                        }
+                }
+                if (t < KK) {  // the odd last tap, its weights in wa0
+                    const f32x4 bias0 = *(const f32x4 *)(bl + (b * KK + t) * 16 + 4 * g);
+                    float x0[4][4];
+                    read_x(t, x0);
+                    f32x4 acc0[4];
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) acc0[pb] = bias0;
+#pragma unroll
+                    for (int q = 0; q < KQ; ++q) G::mma(acc0, wa0[q], bres[q]);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+#pragma unroll
+                        for (int pb = 0; pb < 4; ++pb) {
+                            const bf16x2_t qp = bf16x2_t{(__bf16)acc0[pb][v], (__bf16)0.f};
+                            const uint32_t xp = __float_as_uint(x0[v][pb]) >> 16;
+                            oacc[b][v][pb] = __builtin_amdgcn_fdot2_f32_bf16(qp, __builtin_bit_cast(bf16x2_t, xp),
+                                                                             oacc[b][v][pb], false);
+                        }
+                }
+            };
+            if (full)
+                run_pairs(std::true_type{});
+            else
+                run_pairs(std::false_type{});
+            store_branch(b, oacc[b]);
+            continue;
+        }
         typename G::AFrag anext[KQ > 0 ? KQ : 1];
         if constexpr (KQ > 0) fetch(0, anext);
 #pragma unroll 1
