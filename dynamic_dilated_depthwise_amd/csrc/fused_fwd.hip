@@ -12,6 +12,8 @@
 //   (see gen_mma.hpp), adds the bias, rounds the taps to the dtype, and
 //   multiplies them with x at the dilated offset, read from an LDS copy of the
 //   x tile with its 5*(K-1)/2 halo.  The three branch sums stay in registers.
+//   bfloat16 takes the taps of a branch in pairs and adds each pair's two products
+//   with one v_dot2_f32_bf16.
 // bfloat16 grids with one workgroup per CU instead run workgroups of three such
 // four-wave groups, one per dilation branch, sharing the staged x tile.
 // y is read once per wave into registers (the MFMA B operand is the same for
