@@ -530,15 +530,27 @@ bool bwd_dy_rows_applies(int C, int H, int W, bool al, bool bf16) {
 }
 
 // bfloat16: 256-pixel segments x all 64 output channels when rows are wider than 128
-// pixels and that grid gives every CU a segment; otherwise 128-pixel segments x 32
-// output channels, the two halves of a segment in neighbouring workgroups.
-static bool dy_bf16_wide(int N, int H, int W) {
-    return W > 128 && (int64_t)N * H * ((W + 255) / 256) >= 256;
+// pixels and that grid gives every CU a segment; else 128-pixel segments x 32 output
+// channels (the two halves of a segment in neighbouring workgroups) when that grid
+// does; else 64-pixel segments x 16 output channels (two waves, the four quarters in
+// neighbouring workgroups, each forming its segment's dK itself), which brings grids
+// too small for the halves to the row-staged kernel (64 x 64 at K = 3: 49 -> 28 us
+// against the general kernel) but loses to the halves where both apply (128 x 128:
+// 35 -> 42 us).
+enum DyVariant { kDyWide, kDyHalf, kDyQuarter };
+static DyVariant dy_bf16_variant(int N, int H, int W) {
+    if (W > 128 && (int64_t)N * H * ((W + 255) / 256) >= 256) return kDyWide;
+    if ((int64_t)N * H * ((W + 127) / 128) * 2 >= 256) return kDyHalf;
+    return kDyQuarter;
 }
 
 int64_t bwd_dy_rows_blocks(int N, int H, int W, bool bf16) {
     if (!bf16) return (int64_t)N * H * ((W + kSegY - 1) / kSegY);
-    return dy_bf16_wide(N, H, W) ? (int64_t)N * H * ((W + 255) / 256) : (int64_t)N * H * ((W + 127) / 128) * 2;
+    switch (dy_bf16_variant(N, H, W)) {
+        case kDyWide: return (int64_t)N * H * ((W + 255) / 256);
+        case kDyHalf: return (int64_t)N * H * ((W + 127) / 128) * 2;
+        default: return (int64_t)N * H * ((W + 63) / 64) * 4;
+    }
 }
 
 template <int K, int SEG, int NCP>
@@ -555,10 +567,11 @@ static hipError_t launch_dy_bf16(dim3 grid, const void *x, const void *wg, const
 }
 
 template <int K>
-static hipError_t launch_dy_bf16_k(dim3 grid, bool wide, const void *x, const void *wg, const void *gout, void *gy,
-                                   int H, int W, hipStream_t stream) {
-    if (wide) return launch_dy_bf16<K, 256, 64>(grid, x, wg, gout, gy, H, W, stream);
-    return launch_dy_bf16<K, 128, 32>(grid, x, wg, gout, gy, H, W, stream);
+static hipError_t launch_dy_bf16_k(dim3 grid, DyVariant var, const void *x, const void *wg, const void *gout,
+                                   void *gy, int H, int W, hipStream_t stream) {
+    if (var == kDyWide) return launch_dy_bf16<K, 256, 64>(grid, x, wg, gout, gy, H, W, stream);
+    if (var == kDyHalf) return launch_dy_bf16<K, 128, 32>(grid, x, wg, gout, gy, H, W, stream);
+    return launch_dy_bf16<K, 64, 16>(grid, x, wg, gout, gy, H, W, stream);
 }
 
 hipError_t launch_bwd_dy_rows(const void *x, const void *wg, const void *gout, void *gy, int N, int H, int W, int K,
@@ -567,11 +580,11 @@ hipError_t launch_bwd_dy_rows(const void *x, const void *wg, const void *gout, v
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)nblk), block(256);
     if (bf16) {
-        const bool wide = dy_bf16_wide(N, H, W);
+        const DyVariant var = dy_bf16_variant(N, H, W);
         switch (K) {
-            case 1: return launch_dy_bf16_k<1>(grid, wide, x, wg, gout, gy, H, W, stream);
-            case 3: return launch_dy_bf16_k<3>(grid, wide, x, wg, gout, gy, H, W, stream);
-            default: return launch_dy_bf16_k<5>(grid, wide, x, wg, gout, gy, H, W, stream);
+            case 1: return launch_dy_bf16_k<1>(grid, var, x, wg, gout, gy, H, W, stream);
+            case 3: return launch_dy_bf16_k<3>(grid, var, x, wg, gout, gy, H, W, stream);
+            default: return launch_dy_bf16_k<5>(grid, var, x, wg, gout, gy, H, W, stream);
         }
     }
     const float *X = (const float *)x, *Wg = (const float *)wg, *G = (const float *)gout;

@@ -70,6 +70,11 @@ BWD_CASES = [
     # two at K = 1 with a ragged 136-column row
     ("c64_k5_w200_tall", (S_(1, 64, 264, 200, 5), 223)), ("c64_w264_two_seg", (S_(1, 64, 130, 264, 3), 224)),
     ("c64_k1_batch2_w136", (S_(2, 64, 128, 136, 1), 225)),
+    # C = 64 grids too small for the 128-pixel halves (the bf16 dY quarters: 64-pixel
+    # segments x 16 output channels): one segment per row, a ragged second segment at
+    # K = 5, and K = 1 with a ragged 120-column row
+    ("c64_64_quarters", (S_(1, 64, 64, 64, 3), 226)), ("c64_k5_w96_quarters", (S_(1, 64, 96, 96, 5), 227)),
+    ("c64_k1_w120_quarters", (S_(1, 64, 40, 120, 1), 228)),
 ]
 
 
