@@ -24,9 +24,8 @@ materialised path, ``None`` (the default) picks the fused path when it is eligib
 and the token count N*H*W reaches the threshold for (mode, dtype, K) in
 ``AUTO_MIN_TOKENS``.  The page's thresholds were tuned on its own GPU; these come
 from timing both paths on MI355X (``bench_module.py``, B=1, C=64, 16^2 .. 256^2):
-training is fused at every size with K = 3, from 96^2 = 9216 tokens with K = 5 in
-fp32 and from 128^2 = 16384 tokens with K = 5 in bfloat16, and inference is fused
-at every size.  The fused path also needs about a tenth of the
+training is fused at every size with K = 3 and in bfloat16, from 96^2 = 9216
+tokens with K = 5 in fp32, and inference is fused at every size.  The fused path also needs about a tenth of the
 temporary memory (the tap tensor and its gradient are never stored).
 
 CPU tensors take the CPU path of ``cpu_stream`` (section "CPU 与超大输入": one
@@ -50,7 +49,7 @@ __all__ = ["DDPMFused", "DDPMFilter", "ddpm_fused", "ddpm_filter", "choose_path"
 _F32, _BF16 = torch.float32, torch.bfloat16
 AUTO_MIN_TOKENS = {
     ("train", _F32, 3): 1, ("train", _F32, 5): 9216,
-    ("train", _BF16, 3): 1, ("train", _BF16, 5): 16384,
+    ("train", _BF16, 3): 1, ("train", _BF16, 5): 1,
     ("infer", _F32, 3): 1, ("infer", _F32, 5): 1,
     ("infer", _BF16, 3): 1, ("infer", _BF16, 5): 1,
 }

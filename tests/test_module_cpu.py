@@ -13,7 +13,7 @@ def test_thresholds_table():
             for K in (3, 5):
                 assert (mode, dt, K) in AUTO_MIN_TOKENS
     assert auto_min_tokens(True, F32, 1) == auto_min_tokens(True, F32, 3)
-    assert auto_min_tokens(True, BF16, 5) == 16384  # measured: fused faster from 128^2
+    assert auto_min_tokens(True, BF16, 5) == 1      # measured: fused faster at every size
     assert auto_min_tokens(True, F32, 5) == 9216    # measured: fused faster from 96^2
     assert auto_min_tokens(True, F32, 3) == 1       # measured: fused faster at every size
 
@@ -38,9 +38,8 @@ def test_training_path():
     assert choose_path(True, 9216, 5, F32, F32, F32, False) == "fused"
     assert choose_path(True, 9215, 5, F32, F32, F32, False) == "materialised"
     assert choose_path(True, 100, 3, BF16, BF16, BF16, False) == "fused"
-    assert choose_path(True, 100, 5, BF16, BF16, BF16, False) == "materialised"
-    assert choose_path(True, 16384, 5, BF16, BF16, BF16, False) == "fused"
-    assert choose_path(True, 16383, 5, BF16, BF16, BF16, False) == "materialised"
+    assert choose_path(True, 100, 5, BF16, BF16, BF16, False) == "fused"
+    assert choose_path(True, 100, 5, BF16, BF16, BF16, False, min_tokens=101) == "materialised"
     assert choose_path(True, big, 5, BF16, BF16, BF16, False) == "fused"
     assert choose_path(True, big, 3, F32, F32, F32, True) == "materialised"           # autocast
     assert choose_path(True, big, 3, F32, F32, BF16, False) == "materialised"         # dtype mismatch
