@@ -194,19 +194,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
     // ---- weight fragments of tap (b, t): row o = (b*C + c)*KK + t, columns 32 sub +
     // 8g .. +7, and the row's bias, by buffer loads whose tap part is a constant
     // offset.  A ring of four: the taps of the current pair and of the next.
-    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wg, 3 * C * KK * C * 2);
-    const __amdgpu_buffer_rsrc_t rb = buf_rsrc(bg, 3 * C * KK * 2);
+    // One resource per branch: a tap's part of the offset, t*C*2 (+64) bytes, fits the
+    // instructions' 12-bit immediate offset, so no scalar constant is set per load.
+    const __amdgpu_buffer_rsrc_t rw0 = buf_rsrc(wg, C * KK * C * 2);
+    const __amdgpu_buffer_rsrc_t rw1 = buf_rsrc(wg + C * KK * C, C * KK * C * 2);
+    const __amdgpu_buffer_rsrc_t rw2 = buf_rsrc(wg + 2 * C * KK * C, C * KK * C * 2);
+    const __amdgpu_buffer_rsrc_t rb0 = buf_rsrc(bg, C * KK * 2);
+    const __amdgpu_buffer_rsrc_t rb1 = buf_rsrc(bg + C * KK, C * KK * 2);
+    const __amdgpu_buffer_rsrc_t rb2 = buf_rsrc(bg + 2 * C * KK, C * KK * 2);
     const unsigned wvo = (unsigned)(c * KK * C + 8 * g) * 2u;
     const unsigned bvo = (unsigned)(c * KK) * 2u;
     struct WOps { bf16x8 b0, b1; uint16_t bias; };
     WOps wring[4];
-    auto fetch_w = [&](int bt, WOps &o) {  // bt = b*KK + t
+    auto fetch_w = [&](int bt, WOps &o) {  // bt = b*KK + t (a constant once unrolled)
         const int b = bt / KK;
         const int t = bt - b * KK;
-        const int wso = (b * C * KK + t) * C * 2;
-        o.b0 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo, wso, 0));
-        o.b1 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo, wso + 64, 0));
-        o.bias = __builtin_amdgcn_raw_buffer_load_b16(rb, bvo, (b * C * KK + t) * 2, 0);
+        const __amdgpu_buffer_rsrc_t rw = b == 0 ? rw0 : (b == 1 ? rw1 : rw2);
+        const __amdgpu_buffer_rsrc_t rb = b == 0 ? rb0 : (b == 1 ? rb1 : rb2);
+        o.b0 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo + t * C * 2, 0, 0));
+        o.b1 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, wvo + t * C * 2 + 64, 0, 0));
+        o.bias = __builtin_amdgcn_raw_buffer_load_b16(rb, bvo + t * 2, 0, 0);
     };
     // A fragment (y): plane 4*sub + g, pixel 16pb + i + (LP - dc)
     const int a_lane = g * P::PLANE + i * 16;

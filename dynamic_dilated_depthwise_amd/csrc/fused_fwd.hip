@@ -272,9 +272,15 @@ __global__ __launch_bounds__(GRP3 ? 768 : 256, GRP3 ? 3 : 2) void fused_fwd_kern
                 constexpr bool FULL = decltype(fullc)::value;
                 auto fetch2 = [&](int t, typename G::AFrag (&af)[KQ]) {
                     if constexpr (FULL) {
-                        const T *wbt = wg + ((int64_t)b * C * KK + t) * C;
+                        // a buffer load: the lane's part of the offset is fixed, the
+                        // tap's part a scalar (no 64-bit address arithmetic per tap)
+                        const __amdgpu_buffer_rsrc_t rw =
+                            __builtin_amdgcn_make_buffer_rsrc((void *)wg, 0, 3 * C * KK * C * 2, 0x00020000);
+                        const int so = (b * C * KK + t) * C * 2;
 #pragma unroll
-                        for (int q = 0; q < KQ; ++q) af[q] = G::load_A_off(wbt, aoff + G::CH * q);
+                        for (int q = 0; q < KQ; ++q)
+                            af[q].v = __builtin_bit_cast(
+                                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, (unsigned)(aoff + G::CH * q) * 2u, so, 0));
                     } else {
                         const T *arow = cA < C ? wg + ((int64_t)(b * C + cA) * KK + t) * C : nullptr;
 #pragma unroll
