@@ -576,7 +576,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
 #pragma clang loop unroll(full)
         for (int kj = 0; kj < K; ++kj) {
             const int ti = st * K + kj;  // position in the tap order
-            const int bt = b * KK + ki * K + kj;
             const WOps &cur = ring[ti & 1];
             if (ti + 1 < NT) {
                 const int sn = (kj + 1 < K) ? st : st + 1;

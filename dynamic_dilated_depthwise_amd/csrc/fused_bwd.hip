@@ -16,7 +16,6 @@
 
 namespace ddpm {
 
-constexpr int kRows = 4;   // one row per wave
 constexpr int kCUs = 256;  // compute units of the chip (MI355X)
 constexpr int kCols = 64;  // 16 lanes x 4 pixels
 
