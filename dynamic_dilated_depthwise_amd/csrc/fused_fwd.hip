@@ -39,7 +39,12 @@ template <int K> struct XTile {
     static constexpr int PLANE = LH * LW;
     static constexpr int NV = 16 * PLANE / 4;          // 4-column runs of the 16-channel tile
     static constexpr int BIAS = 3 * K * K * 16;  // bias of the 16 channels for every (b, t)
-    static constexpr size_t bytes = sizeof(float) * (16 * PLANE + BIAS);
+    static constexpr int BOFF = 16 * PLANE + 4;  // where the bias slice starts (floats)
+    static constexpr size_t bytes = sizeof(float) * (BOFF + BIAS);
+    // Plane of channel ch.  A wave reads channel 4g+v in lane group g at columns 4j+..,
+    // and 4*PLANE is a multiple of the 64 banks, so the four groups would hit the same
+    // 16 banks; shifting group g's planes by g floats spreads them over all 64.
+    static __device__ __forceinline__ int plane(int ch) { return ch * PLANE + (ch >> 2); }
 };
 
 // Stage x[n, c0..c0+15, h0-HALO .., w0-PADC ..] into LDS as float, zero outside the
@@ -86,7 +91,12 @@ __device__ __forceinline__ void stage_x_tile(float *xs, const T *__restrict__ xn
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
                 const int i = (k0 + k) * NT + (int)threadIdx.x;
-                if (k0 + k < IT && i < X::NV) *(f32x4 *)(xs + 4 * i) = v[k];
+                if (k0 + k < IT && i < X::NV) {
+                    // shifted planes: 4-byte aligned, two ds_write2_b32
+                    float *d = xs + 4 * i + (i / (X::NV / 4));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) d[e] = v[k][e];
+                }
             }
         }
     } else {
@@ -114,7 +124,7 @@ __device__ __forceinline__ void stage_x_tile(float *xs, const T *__restrict__ xn
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
                 const int i = (k0 + k) * NT + (int)threadIdx.x;
-                if (k0 + k < IT && i < NE) xs[i] = v[k];
+                if (k0 + k < IT && i < NE) xs[i + i / (NE / 4)] = v[k];
             }
         }
     }
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(GRP3 ? 768 : 256, GRP3 ? 3 : 2) void fused_fwd_kern
     const T *__restrict__ xn = x + (int64_t)n * C * HW;
     const T *__restrict__ yn = y + (int64_t)n * C * HW;
     // bias slice: bl[(b*KK + t)*16 + ch] = bias[(b*C + c0 + ch)*KK + t]
-    float *bl = xs + 16 * X::PLANE;
+    float *bl = xs + X::BOFF;
     if (!GRP3 || wave_all < 4) {  // the first 256 threads stage the shared tile
         stage_x_tile<T, K>(xs, xn, c0, C, H, W, HW, h0, w0, aligned4);
 #pragma unroll
@@ -224,7 +234,8 @@ __global__ __launch_bounds__(GRP3 ? 768 : 256, GRP3 ? 3 : 2) void fused_fwd_kern
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int c = c0 + 4 * g + v;
-            const f32x4 xv = *(const f32x4 *)(xs + (4 * g + v) * X::PLANE + (wave + X::HALO) * X::LW + X::PADC + 4 * j);
+            const float *xp = xs + X::plane(4 * g + v) + (wave + X::HALO) * X::LW + X::PADC + 4 * j;
+            const f32x4 xv = {xp[0], xp[1], xp[2], xp[3]};
             if (c < C) store4_bits(on + (int64_t)c * HW + rowoff, w, W, xv, aligned4);
         }
     }
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(GRP3 ? 768 : 256, GRP3 ? 3 : 2) void fused_fwd_kern
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
 #pragma unroll
-                        for (int pb = 0; pb < 4; ++pb) xv[v][pb] = xl[(4 * g + v) * X::PLANE + pb];
+                        for (int pb = 0; pb < 4; ++pb) xv[v][pb] = xl[X::plane(4 * g + v) + pb];
                 };
                 typename G::AFrag wa0[KQ], wa1[KQ];
                 fetch2(0, wa0);
@@ -384,7 +395,7 @@ __global__ __launch_bounds__(GRP3 ? 768 : 256, GRP3 ? 3 : 2) void fused_fwd_kern
             const float *xl = xs + (wave + X::HALO + (ki - r) * D) * X::LW + 4 * j + X::PADC + (kj - r) * D;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float *xr = xl + (4 * g + v) * X::PLANE;
+                const float *xr = xl + X::plane(4 * g + v);
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) oacc[b][v][pb] += Elem<T>::quant(acc[pb][v]) * xr[pb];
             }
@@ -448,6 +459,8 @@ static hipError_t launch_fused_k(const void *x, const void *y, const void *wg, c
 
 hipError_t launch_fused_fwd(const void *x, const void *y, const void *wg, const void *bg, void *out, int N, int C,
                             int H, int W, int K, bool bf16, bool al, hipStream_t stream) {
+    if (fused_fwd_pers_applies(N, C, H, W, K, bf16, al))
+        return launch_fused_fwd_pers(x, y, wg, bg, out, N, H, W, stream);
     if (bf16) {
         switch (K) {
             case 1: return launch_fused_k<bf16_t, 1>(x, y, wg, bg, out, N, C, H, W, al, stream);

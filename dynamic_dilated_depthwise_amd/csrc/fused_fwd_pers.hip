@@ -1,0 +1,392 @@
+// fused_fwd_pers.hip -- bfloat16 fused forward for K = 3 and C = 64 as persistent
+// workgroups that stream their tiles into LDS (gfx950).
+//
+// Operation and arithmetic are those of the bfloat16 path in fused_fwd.hip (page
+// "lartpang/DynamicConvolutionOperator", section "CUDA 融合生成器推理"): per 16-channel
+// block and 4 x 64 pixel tile the 1x1 generator (MFMA 16x16x32 bf16 over the 64 input
+// channels, bias added, each tap rounded to bf16) gives the dynamic taps, and each
+// branch's output sums tap x shifted x over the taps, in pairs through
+// v_dot2_f32_bf16, in the same order: the outputs are bit-identical.
+//
+// What differs is how the work reaches the CU.  The per-tile kernel stages every tile
+// at the same moment in every workgroup and then computes, so its memory phase and
+// its tap loop do not overlap.  Here one workgroup of 12 waves per CU keeps one
+// channel block and walks a run of spatial tiles:
+//   * its 432 generator rows (3 branches x 9 taps x 16 channels x 64 inputs, 55 KB)
+//     and biases are loaded into LDS once;
+//   * the next tile's x (16 channels x 14 rows x 80 columns of raw bf16, 35 KB, two
+//     buffers) and y (64 channels x 4 rows x 64 columns, 32 KB) are fetched with
+//     direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) while the current tile
+//     is computed.  They take no registers, and nothing in the tap loop waits on
+//     vector memory: weights, biases and x values all come from LDS;
+//   * wave w computes branch w / 4 of tile row w % 4 (the three branches share the
+//     x tile).
+// Rows and 16-byte column runs outside the image read zero (a buffer offset past
+// the end).  Outputs are buffer stores, one instruction per channel whatever the
+// lanes' bounds, so every wave knows how many stores follow its loads of the next
+// tile and waits for those loads alone.
+#include <algorithm>
+#include <type_traits>
+
+#include "gen_mma.hpp"
+#include "launchers.hpp"
+
+namespace ddpm {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct PT {
+    static constexpr int C = 64;
+    static constexpr int KK = 9;
+    static constexpr int HALO = 5;                 // 5 * (K - 1) / 2
+    static constexpr int LH = 4 + 2 * HALO;        // 14 staged rows
+    static constexpr int CHUNKS = 10;              // 16-byte runs per staged row: columns w0-8 .. w0+71
+    static constexpr int ROWB = CHUNKS * 16;       // 160 bytes
+    static constexpr int PLANEB = LH * ROWB;       // 2240 bytes per channel
+    static constexpr int XSLOTS = 16 * LH * CHUNKS;  // 2240 runs
+    static constexpr int XLOADS = XSLOTS / 64;       // 35 wave loads
+    static constexpr int YSLOTS = C * 4 * 8;         // 2048 runs
+    static constexpr int YLOADS = YSLOTS / 64;       // 32
+    static constexpr int WROWS = 3 * KK * 16;        // 432 rows of 64 bf16
+    static constexpr int WLOADS = WROWS * 8 / 64;    // 54
+    static constexpr int OFF_W = 0;
+    static constexpr int OFF_X = WROWS * 128;        // two x buffers
+    static constexpr int XBUF = XSLOTS * 16;
+    static constexpr int OFF_Y = OFF_X + 2 * XBUF;
+    static constexpr int OFF_B = OFF_Y + YSLOTS * 16;
+    static constexpr int BYTES = OFF_B + WROWS * 4;  // 161472
+    static constexpr int WAVES = 12;
+};
+static_assert(PT::XSLOTS % 64 == 0 && PT::YSLOTS % 64 == 0 && (PT::WROWS * 8) % 64 == 0, "whole wave loads");
+static_assert(PT::BYTES <= 160 * 1024, "one CU's LDS");
+static_assert(PT::XLOADS <= 3 * PT::WAVES && PT::YLOADS <= 3 * PT::WAVES && PT::WLOADS <= 5 * PT::WAVES, "loads per wave");
+
+constexpr unsigned kOobOff = 0x7ffffff0u;  // past any buffer this kernel takes: reads zero, stores dropped
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from buffer offset voff to lds + 16 * lane (lds wave-uniform)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, unsigned voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, 0, 0, 0);
+}
+// Workgroup barrier after this wave's LDS reads have returned and all but its last
+// VM vector-memory operations have completed (the direct-to-LDS loads before them have
+// then written LDS).  One asm statement with a memory clobber: no memory access moves
+// across it, and it waits on nothing else (a fence would also wait for the loads of
+// the next tile that are still in flight).
+template <int VM> __device__ __forceinline__ void barrier_after() {
+    static_assert(VM == 0 || VM == 4 || VM == 8 || VM == 63, "vmcnt");
+    if constexpr (VM == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (VM == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (VM == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (VM == 63) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+template <int V> using IC = std::integral_constant<int, V>;
+
+__global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__restrict__ x,
+                                                                const bf16_t *__restrict__ y,
+                                                                const bf16_t *__restrict__ wg,
+                                                                const bf16_t *__restrict__ bg, bf16_t *__restrict__ out,
+                                                                int N, int H, int W, unsigned xbytes,
+                                                                unsigned obytes) {
+    constexpr int C = PT::C, KK = PT::KK;
+    extern __shared__ __align__(16) char sm[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = wave_all >> 2;    // branch of this wave
+    const int wave = wave_all & 3;  // tile row of this wave
+    const int D = dilation(b);
+    const int g = lane >> 4, j = lane & 15;
+    const int HW = H * W;
+    const int ncolt = (W + 63) / 64, nbands = (H + 3) / 4;
+    const int S = N * nbands * ncolt;  // spatial tiles
+    constexpr int nCB = C / 16;
+    const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int c0 = (L % nCB) * 16;
+    const int m = L / nCB, per = gridDim.x / nCB;  // this workgroup's tiles: m, m + per, ...
+
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x, xbytes), ry = rsrc(y, xbytes);
+    const __amdgpu_buffer_rsrc_t rw = rsrc(wg, 3u * C * KK * C * 2u), ro = rsrc(out, obytes);
+
+    // The channel block's generator rows, row r = (branch * 9 + tap) * 16 + channel, its
+    // 16-byte runs XOR-swizzled by (channel / 2) & 7 so that the 16 rows an A-operand
+    // read touches per lane group fall on distinct banks.
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const int i = wave_all + PT::WAVES * k;
+        if (i < PT::WLOADS) {
+            const int s = i * 64 + lane;
+            const int r = s >> 3, pos = s & 7;
+            const int bt = r >> 4, ch = r & 15;
+            const int bb = bt / KK, t = bt - KK * bb;
+            const int run = pos ^ ((ch >> 1) & 7);
+            dma16(rw, sm + PT::OFF_W + i * 1024, (unsigned)((((bb * C + c0 + ch) * KK + t) * C + run * 8) * 2));
+        }
+    }
+    if (tid < PT::WROWS) {  // biases, widened: [branch * 9 + tap][channel]
+        const int bt = tid >> 4, ch = tid & 15;
+        const int bb = bt / KK, t = bt - KK * bb;
+        ((float *)(sm + PT::OFF_B))[tid] = bf16_bits_to_f32(bg[(bb * C + c0 + ch) * KK + t]);
+    }
+
+    // This wave's share of the x loads: run s = ch * 140 + row * 10 + chunk of the tile.
+    int xrel[3], xrc[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int s = (wave_all + PT::WAVES * k) * 64 + lane;
+        const int ch = s / (PT::LH * PT::CHUNKS);
+        const int rem = s - ch * (PT::LH * PT::CHUNKS);
+        const int row = rem / PT::CHUNKS, chunk = rem - row * PT::CHUNKS;
+        xrel[k] = (ch * HW + (row - PT::HALO) * W + chunk * 8 - 8) * 2;
+        xrc[k] = row | (chunk << 8);
+    }
+    auto tile_of = [&](int st, int &n, int &h0, int &w0) {
+        const int colt = st % ncolt;
+        const int rest = st / ncolt;
+        h0 = (rest % nbands) * 4;
+        n = rest / nbands;
+        w0 = colt * 64;
+    };
+    auto issue_x = [&](int st, int buf) {
+        int n, h0, w0;
+        tile_of(st, n, h0, w0);
+        const int base = ((n * C + c0) * HW + h0 * W + w0) * 2;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int i = wave_all + PT::WAVES * k;
+            if (i < PT::XLOADS) {
+                const int hh = h0 - PT::HALO + (xrc[k] & 0xff);
+                const int ww = w0 - 8 + 8 * (xrc[k] >> 8);
+                const bool ok = (unsigned)hh < (unsigned)H && (unsigned)ww < (unsigned)W;
+                dma16(rx, sm + PT::OFF_X + buf * PT::XBUF + i * 1024, ok ? (unsigned)(base + xrel[k]) : kOobOff);
+            }
+        }
+    };
+    // y runs s = ch * 32 + row * 8 + chunk
+    auto issue_y = [&](int st) {
+        int n, h0, w0;
+        tile_of(st, n, h0, w0);
+        const int base = (n * C * HW + h0 * W + w0) * 2;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int i = wave_all + PT::WAVES * k;
+            if (i < PT::YLOADS) {
+                const int s = i * 64 + lane;
+                const int ch = s >> 5, row = (s >> 3) & 3, chunk = s & 7;
+                const bool ok = h0 + row < H && w0 + 8 * chunk < W;
+                dma16(ry, sm + PT::OFF_Y + i * 1024,
+                      ok ? (unsigned)(base + (ch * HW + row * W + chunk * 8) * 2) : kOobOff);
+            }
+        }
+    };
+
+    // lane parts of the LDS reads
+    const int wl0 = j * 128 + ((g ^ ((j >> 1) & 7)) << 4);        // A operand, k = 8g .. 8g+7
+    const int wl1 = j * 128 + (((4 + g) ^ ((j >> 1) & 7)) << 4);  // k = 32 + 8g ..
+    const int xl = 4 * g * PT::PLANEB + (wave + PT::HALO) * PT::ROWB + (4 * j + 8) * 2;  // channel 4g, pixel 4j
+    const int yl = 8 * g * 512 + wave * 128 + 8 * j;  // channel 8g, this row, pixel 4j
+    const char *wb = sm + PT::OFF_W + b * KK * 2048;
+    const float *bl = (const float *)(sm + PT::OFF_B) + b * KK * 16 + 4 * g;
+
+    issue_x(m, 0);
+    issue_y(m);
+    int it = 0;
+#pragma unroll 1
+    for (int st = m; st < S; st += per, ++it) {
+        // Every wave's loads of this tile have landed (the stores of the previous tile,
+        // issued after them, may still be in flight), and every wave is done with the
+        // previous tile's x buffer.
+        if (it == 0)
+            barrier_after<0>();
+        else if (b == 0)
+            barrier_after<8>();
+        else
+            barrier_after<4>();
+        const int buf = it & 1;
+        const int nxt = st + per;
+        if (nxt < S) issue_x(nxt, buf ^ 1);
+
+        // the generator's B operand: y of this row, channels 32q + 8g + e, pixel 4j + pb
+        Gen<bf16_t>::BFrag bres[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            u32x2_t r[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] = *(const u32x2_t *)(sm + PT::OFF_Y + yl + (32 * q + e) * 512);
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                u32x4_t d;
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm)
+                    d[mm] = __builtin_amdgcn_perm(r[2 * mm + 1][pb >> 1], r[2 * mm][pb >> 1],
+                                                  (pb & 1) ? 0x07060302u : 0x05040100u);
+                bres[q].v[pb] = __builtin_bit_cast(bf16x8, d);
+            }
+        }
+        barrier_after<63>();  // every wave holds its y operand before the next tile's y lands
+        if (nxt < S) issue_y(nxt);
+
+        const char *xb = sm + PT::OFF_X + buf * PT::XBUF + xl;
+        // x of tap t at pixel 4j + pb, channel 4g + v: dwords at an aligned start, the
+        // half of each known at compile time (the dilations are odd, so the column
+        // offset's parity is that of kj - 1)
+        auto read_x = [&](auto tc, uint32_t (&d)[4][3]) {
+            constexpr int t = decltype(tc)::value;
+            constexpr int ki = t / 3, kj = t % 3;
+            constexpr bool odd = kj != 1;
+            const char *p = xb + (ki - 1) * D * PT::ROWB + (kj - 1) * D * 2 - (odd ? 2 : 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                if constexpr (odd) {
+                    const uint32_t *q = (const uint32_t *)(p + v * PT::PLANEB);
+                    d[v][0] = q[0]; d[v][1] = q[1]; d[v][2] = q[2];
+                } else {
+                    const u32x2_t e = *(const u32x2_t *)(p + v * PT::PLANEB);
+                    d[v][0] = e[0]; d[v][1] = e[1]; d[v][2] = 0;
+                }
+            }
+        };
+        auto read_w = [&](auto tc, bf16x8 (&a)[2]) {
+            constexpr int t = decltype(tc)::value;
+            a[0] = *(const bf16x8 *)(wb + t * 2048 + wl0);
+            a[1] = *(const bf16x8 *)(wb + t * 2048 + wl1);
+        };
+        float oacc[4][4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) oacc[v][pb] = 0.f;
+        auto pair = [&](auto t0c) {
+            constexpr int t0 = decltype(t0c)::value, t1 = t0 + 1;
+            constexpr bool odd0 = (t0 % 3) != 1, odd1 = (t1 % 3) != 1;
+            bf16x8 a0[2], a1[2];
+            read_w(IC<t0>{}, a0);
+            read_w(IC<t1>{}, a1);
+            const f32x4 bias0 = *(const f32x4 *)(bl + t0 * 16);
+            const f32x4 bias1 = *(const f32x4 *)(bl + t1 * 16);
+            uint32_t x0[4][3], x1[4][3];
+            read_x(IC<t0>{}, x0);
+            read_x(IC<t1>{}, x1);
+            f32x4 acc0[4], acc1[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                acc0[pb] = bias0;
+                acc1[pb] = bias1;
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc0[pb] = mfma_16x16x32_bf16(a0[q], bres[q].v[pb], acc0[pb]);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc1[pb] = mfma_16x16x32_bf16(a1[q], bres[q].v[pb], acc1[pb]);
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int i0 = odd0 ? (pb + 1) >> 1 : pb >> 1, i1 = odd1 ? (pb + 1) >> 1 : pb >> 1;
+                const bool hi0 = odd0 ? ((pb + 1) & 1) : (pb & 1), hi1 = odd1 ? ((pb + 1) & 1) : (pb & 1);
+                const uint32_t sel = (hi0 ? 0x0302u : 0x0100u) | (hi1 ? 0x07060000u : 0x05040000u);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bf16x2_t qp = bf16x2_t{(__bf16)acc0[pb][v], (__bf16)acc1[pb][v]};
+                    const uint32_t xp = __builtin_amdgcn_perm(x1[v][i1], x0[v][i0], sel);
+                    oacc[v][pb] = __builtin_amdgcn_fdot2_f32_bf16(qp, __builtin_bit_cast(bf16x2_t, xp), oacc[v][pb],
+                                                                  false);
+                }
+            }
+        };
+        pair(IC<0>{});
+        pair(IC<2>{});
+        pair(IC<4>{});
+        pair(IC<6>{});
+        {  // the odd last tap, paired with zeros
+            constexpr int t = 8;
+            bf16x8 a0[2];
+            read_w(IC<t>{}, a0);
+            const f32x4 bias0 = *(const f32x4 *)(bl + t * 16);
+            uint32_t x0[4][3];
+            read_x(IC<t>{}, x0);
+            f32x4 acc0[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc0[pb] = bias0;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc0[pb] = mfma_16x16x32_bf16(a0[q], bres[q].v[pb], acc0[pb]);
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int i0 = (pb + 1) >> 1;  // kj = 2: odd
+                const bool hi = ((pb + 1) & 1) != 0;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bf16x2_t qp = bf16x2_t{(__bf16)acc0[pb][v], (__bf16)0.f};
+                    const uint32_t xp = hi ? (x0[v][i0] >> 16) : (x0[v][i0] & 0xffffu);
+                    oacc[v][pb] = __builtin_amdgcn_fdot2_f32_bf16(qp, __builtin_bit_cast(bf16x2_t, xp), oacc[v][pb],
+                                                                  false);
+                }
+            }
+        }
+
+        // Outputs: 4 stores for the branch, 4 more for the x block in branch-0 waves.
+        int n, h0, w0;
+        tile_of(st, n, h0, w0);
+        const int h = h0 + wave, w = w0 + 4 * j;
+        const bool ok = h < H && w < W;  // W % 8 == 0: a pixel quad is whole or absent
+        const int pix = h * W + w;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int c = c0 + 4 * g + v;
+            const u32x2_t d = {pack_rne(oacc[v][0], oacc[v][1]), pack_rne(oacc[v][2], oacc[v][3])};
+            const int off = (((n * 4 + 1 + b) * C + c) * HW + pix) * 2;
+            __builtin_amdgcn_raw_buffer_store_b64(d, ro, ok ? (unsigned)off : kOobOff, 0, 0);
+        }
+        if (b == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int c = c0 + 4 * g + v;
+                const u32x2_t d = *(const u32x2_t *)(xb + v * PT::PLANEB);
+                const int off = ((n * 4 * C + c) * HW + pix) * 2;
+                __builtin_amdgcn_raw_buffer_store_b64(d, ro, ok ? (unsigned)off : kOobOff, 0, 0);
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+}  // namespace
+
+bool fused_fwd_pers_applies(int N, int C, int H, int W, int K, bool bf16, bool al) {
+    if (!bf16 || K != 3 || C != 64 || !al || W % 8 != 0 || N <= 0 || H <= 0 || W <= 0) return false;
+    const int64_t HW = (int64_t)H * W;
+    const int64_t xbytes = (int64_t)N * C * HW * 2, obytes = 4 * xbytes;
+    if (obytes >= (int64_t)kOobOff) return false;  // 32-bit buffer offsets, kOobOff past the end
+    const int64_t tiles = (int64_t)N * ((H + 3) / 4) * ((W + 63) / 64) * (C / 16);
+    return tiles >= 512;  // at least two tiles per workgroup on average
+}
+
+hipError_t launch_fused_fwd_pers(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
+                                 int H, int W, hipStream_t stream) {
+    constexpr int C = PT::C;
+    const int64_t S = (int64_t)N * ((H + 3) / 4) * ((W + 63) / 64);
+    constexpr int kCUs = 256;
+    const int per = (int)std::min<int64_t>(S, kCUs / (C / 16));
+    const unsigned xbytes = (unsigned)((int64_t)N * C * H * W * 2);
+    hipError_t e = hipFuncSetAttribute((const void *)fused_fwd_pers_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, PT::BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fused_fwd_pers_kernel, dim3((unsigned)(per * (C / 16))), dim3(64 * PT::WAVES), PT::BYTES,
+                       stream, (const bf16_t *)x, (const bf16_t *)y, (const bf16_t *)wg, (const bf16_t *)bg,
+                       (bf16_t *)out, N, H, W, xbytes, 4u * xbytes);
+    return hipGetLastError();
+}
+
+}  // namespace ddpm

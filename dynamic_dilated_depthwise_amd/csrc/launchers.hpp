@@ -15,6 +15,12 @@ hipError_t launch_filter_fwd(const void *x, const void *taps, void *out, int N, 
 hipError_t launch_fused_fwd(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
                             int C, int H, int W, int K, bool bf16, bool aligned4, hipStream_t stream);
 
+// bfloat16 forward for K = 3, C = 64 as persistent workgroups streaming their tiles
+// into LDS; fused_fwd_pers_applies tells whether a shape can take it.
+bool fused_fwd_pers_applies(int N, int C, int H, int W, int K, bool bf16, bool al);
+hipError_t launch_fused_fwd_pers(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,
+                                 int H, int W, hipStream_t stream);
+
 // gx, gy or (dw_part, db_part) may be null: that part is skipped.
 hipError_t launch_fused_bwd(const void *x, const void *y, const void *wg, const void *bg, const void *gout,
                             void *gx, void *gy, float *dw_part, float *db_part, int S, int N, int C, int H,
