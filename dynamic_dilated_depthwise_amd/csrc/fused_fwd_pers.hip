@@ -45,9 +45,9 @@ struct PT {
     static constexpr int HALO = 5;                 // 5 * (K - 1) / 2
     static constexpr int LH = 4 + 2 * HALO;        // 14 staged rows
     static constexpr int CHUNKS = 10;              // 16-byte runs per staged row: columns w0-8 .. w0+71
-    static constexpr int ROWB = CHUNKS * 16;       // 160 bytes
-    static constexpr int PLANEB = LH * ROWB;       // 2240 bytes per channel
-    static constexpr int XSLOTS = 16 * LH * CHUNKS;  // 2240 runs
+    static constexpr int CHB = CHUNKS * 16;        // 160 bytes per channel of a staged row
+    static constexpr int ROWB = 16 * CHB;          // 2560 bytes per staged row (16 channels)
+    static constexpr int XSLOTS = LH * 16 * CHUNKS;  // 2240 runs, (row, channel, run) order
     static constexpr int XLOADS = XSLOTS / 64;       // 35 wave loads
     static constexpr int YSLOTS = C * 4 * 8;         // 2048 runs
     static constexpr int YLOADS = YSLOTS / 64;       // 32
@@ -138,67 +138,72 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
         ((float *)(sm + PT::OFF_B))[tid] = bf16_bits_to_f32(bg[(bb * C + c0 + ch) * KK + t]);
     }
 
-    // This wave's share of the x loads: run s = ch * 140 + row * 10 + chunk of the tile.
+    // This wave's share of the x loads: run s = (row * 16 + ch) * 10 + chunk of the
+    // staged tile; xrc packs the run's row and column offsets from (h0, w0).
     int xrel[3], xrc[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const int s = (wave_all + PT::WAVES * k) * 64 + lane;
-        const int ch = s / (PT::LH * PT::CHUNKS);
-        const int rem = s - ch * (PT::LH * PT::CHUNKS);
-        const int row = rem / PT::CHUNKS, chunk = rem - row * PT::CHUNKS;
+        const int row = s / (16 * PT::CHUNKS);
+        const int rem = s - row * (16 * PT::CHUNKS);
+        const int ch = rem / PT::CHUNKS, chunk = rem - ch * PT::CHUNKS;
         xrel[k] = (ch * HW + (row - PT::HALO) * W + chunk * 8 - 8) * 2;
-        xrc[k] = row | (chunk << 8);
+        xrc[k] = ((row - PT::HALO) & 0xffff) | ((chunk * 8 - 8) * 65536);
     }
-    auto tile_of = [&](int st, int &n, int &h0, int &w0) {
-        const int colt = st % ncolt;
-        const int rest = st / ncolt;
-        h0 = (rest % nbands) * 4;
-        n = rest / nbands;
-        w0 = colt * 64;
+    // The tiles m, m + per, ... in (image, row band, column tile) order, walked with
+    // carries instead of divisions.
+    struct Tile { int n, band, colt; };
+    const int dcol = per % ncolt, drest = per / ncolt;
+    const int dband = drest % nbands, dn = drest / nbands;
+    auto advance = [&](Tile t) {
+        t.colt += dcol;
+        if (t.colt >= ncolt) { t.colt -= ncolt; ++t.band; }
+        t.band += dband;
+        if (t.band >= nbands) { t.band -= nbands; ++t.n; }
+        t.n += dn;
+        return t;
     };
-    auto issue_x = [&](int st, int buf) {
-        int n, h0, w0;
-        tile_of(st, n, h0, w0);
-        const int base = ((n * C + c0) * HW + h0 * W + w0) * 2;
+    auto issue_x = [&](Tile tl, int buf) {
+        const int h0 = tl.band * 4, w0 = tl.colt * 64;
+        const int base = ((tl.n * C + c0) * HW + h0 * W + w0) * 2;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             const int i = wave_all + PT::WAVES * k;
             if (i < PT::XLOADS) {
-                const int hh = h0 - PT::HALO + (xrc[k] & 0xff);
-                const int ww = w0 - 8 + 8 * (xrc[k] >> 8);
+                const int hh = h0 + (int)(short)(xrc[k] & 0xffff);
+                const int ww = w0 + (xrc[k] >> 16);
                 const bool ok = (unsigned)hh < (unsigned)H && (unsigned)ww < (unsigned)W;
                 dma16(rx, sm + PT::OFF_X + buf * PT::XBUF + i * 1024, ok ? (unsigned)(base + xrel[k]) : kOobOff);
             }
         }
     };
-    // y runs s = ch * 32 + row * 8 + chunk
-    auto issue_y = [&](int st) {
-        int n, h0, w0;
-        tile_of(st, n, h0, w0);
-        const int base = (n * C * HW + h0 * W + w0) * 2;
+    // y runs s = ch * 32 + row * 8 + chunk: a wave load covers channels 2i, 2i + 1, and
+    // a lane's row and column run are the same in every load
+    const int yrow = (lane >> 3) & 3, ycol = (lane & 7) * 8;
+    const int ylane = ((lane >> 5) * HW + yrow * W + ycol) * 2;
+    auto issue_y = [&](Tile tl) {
+        const int h0 = tl.band * 4, w0 = tl.colt * 64;
+        const bool ok = h0 + yrow < H && w0 + ycol < W;
+        const int base = (tl.n * C * HW + h0 * W + w0) * 2 + ylane;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             const int i = wave_all + PT::WAVES * k;
-            if (i < PT::YLOADS) {
-                const int s = i * 64 + lane;
-                const int ch = s >> 5, row = (s >> 3) & 3, chunk = s & 7;
-                const bool ok = h0 + row < H && w0 + 8 * chunk < W;
-                dma16(ry, sm + PT::OFF_Y + i * 1024,
-                      ok ? (unsigned)(base + (ch * HW + row * W + chunk * 8) * 2) : kOobOff);
-            }
+            if (i < PT::YLOADS)
+                dma16(ry, sm + PT::OFF_Y + i * 1024, ok ? (unsigned)(base + 4 * i * HW) : kOobOff);
         }
     };
 
     // lane parts of the LDS reads
     const int wl0 = j * 128 + ((g ^ ((j >> 1) & 7)) << 4);        // A operand, k = 8g .. 8g+7
     const int wl1 = j * 128 + (((4 + g) ^ ((j >> 1) & 7)) << 4);  // k = 32 + 8g ..
-    const int xl = 4 * g * PT::PLANEB + (wave + PT::HALO) * PT::ROWB + (4 * j + 8) * 2;  // channel 4g, pixel 4j
+    const int xl = (wave + PT::HALO) * PT::ROWB + 4 * g * PT::CHB + (4 * j + 8) * 2;  // channel 4g, pixel 4j
     const int yl = 8 * g * 512 + wave * 128 + 8 * j;  // channel 8g, this row, pixel 4j
     const char *wb = sm + PT::OFF_W + b * KK * 2048;
     const float *bl = (const float *)(sm + PT::OFF_B) + b * KK * 16 + 4 * g;
 
-    issue_x(m, 0);
-    issue_y(m);
+    Tile cur = {m / (ncolt * nbands), (m / ncolt) % nbands, m % ncolt};
+    issue_x(cur, 0);
+    issue_y(cur);
     int it = 0;
 #pragma unroll 1
     for (int st = m; st < S; st += per, ++it) {
@@ -213,7 +218,8 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
             barrier_after<4>();
         const int buf = it & 1;
         const int nxt = st + per;
-        if (nxt < S) issue_x(nxt, buf ^ 1);
+        const Tile tnx = advance(cur);
+        if (nxt < S) issue_x(tnx, buf ^ 1);
 
         // the generator's B operand: y of this row, channels 32q + 8g + e, pixel 4j + pb
         Gen<bf16_t>::BFrag bres[2];
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
             }
         }
         barrier_after<63>();  // every wave holds its y operand before the next tile's y lands
-        if (nxt < S) issue_y(nxt);
+        if (nxt < S) issue_y(tnx);
 
         const char *xb = sm + PT::OFF_X + buf * PT::XBUF + xl;
         // x of tap t at pixel 4j + pb, channel 4g + v: dwords at an aligned start, the
@@ -247,10 +253,10 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 if constexpr (odd) {
-                    const uint32_t *q = (const uint32_t *)(p + v * PT::PLANEB);
+                    const uint32_t *q = (const uint32_t *)(p + v * PT::CHB);
                     d[v][0] = q[0]; d[v][1] = q[1]; d[v][2] = q[2];
                 } else {
-                    const u32x2_t e = *(const u32x2_t *)(p + v * PT::PLANEB);
+                    const u32x2_t e = *(const u32x2_t *)(p + v * PT::CHB);
                     d[v][0] = e[0]; d[v][1] = e[1]; d[v][2] = 0;
                 }
             }
@@ -282,6 +288,9 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
                 acc0[pb] = bias0;
                 acc1[pb] = bias1;
             }
+            // The pair's 16 MFMAs as one block: v_dot2_f32_bf16 shares the matrix core's
+            // issue, and dot products scheduled between dependent MFMAs only stall them.
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -290,6 +299,7 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
             for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) acc1[pb] = mfma_16x16x32_bf16(a1[q], bres[q].v[pb], acc1[pb]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) {
                 const int i0 = odd0 ? (pb + 1) >> 1 : pb >> 1, i1 = odd1 ? (pb + 1) >> 1 : pb >> 1;
@@ -337,8 +347,7 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
         }
 
         // Outputs: 4 stores for the branch, 4 more for the x block in branch-0 waves.
-        int n, h0, w0;
-        tile_of(st, n, h0, w0);
+        const int n = cur.n, h0 = cur.band * 4, w0 = cur.colt * 64;
         const int h = h0 + wave, w = w0 + 4 * j;
         const bool ok = h < H && w < W;  // W % 8 == 0: a pixel quad is whole or absent
         const int pix = h * W + w;
@@ -353,11 +362,12 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int c = c0 + 4 * g + v;
-                const u32x2_t d = *(const u32x2_t *)(xb + v * PT::PLANEB);
+                const u32x2_t d = *(const u32x2_t *)(xb + v * PT::CHB);
                 const int off = ((n * 4 * C + c) * HW + pix) * 2;
                 __builtin_amdgcn_raw_buffer_store_b64(d, ro, ok ? (unsigned)off : kOobOff, 0, 0);
             }
         }
+        cur = tnx;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -368,9 +378,9 @@ bool fused_fwd_pers_applies(int N, int C, int H, int W, int K, bool bf16, bool a
     if (!bf16 || K != 3 || C != 64 || !al || W % 8 != 0 || N <= 0 || H <= 0 || W <= 0) return false;
     const int64_t HW = (int64_t)H * W;
     const int64_t xbytes = (int64_t)N * C * HW * 2, obytes = 4 * xbytes;
-    if (obytes >= (int64_t)kOobOff) return false;  // 32-bit buffer offsets, kOobOff past the end
-    const int64_t tiles = (int64_t)N * ((H + 3) / 4) * ((W + 63) / 64) * (C / 16);
-    return tiles >= 512;  // at least two tiles per workgroup on average
+    // 32-bit buffer offsets with kOobOff past the end.  No lower bound on the grid:
+    // even a grid of a few tiles runs faster than the per-tile kernel.
+    return obytes < (int64_t)kOobOff;
 }
 
 hipError_t launch_fused_fwd_pers(const void *x, const void *y, const void *wg, const void *bg, void *out, int N,

@@ -43,10 +43,12 @@ FWD_CASES = [
     ("w256_k5", (S_(1, 6, 13, 256, 5), 118)), ("w264_k1", (S_(2, 5, 3, 264, 1), 119)),
     # a batch of four mid-size images on the workload's channel count (full-size grids)
     ("batch4_c64_64", (S_(4, 64, 64, 64, 3), 117)),
-    # bfloat16 K = 3, C = 64 grids of 512+ tiles (the persistent forward): ragged last
-    # row band and column tile in a batch of two with uneven tile runs per workgroup,
-    # and a batch of three with an 8-column last tile
+    # bfloat16 K = 3, C = 64 with W % 8 == 0 (the persistent forward): ragged last row
+    # band and column tile in a batch of two with uneven tile runs per workgroup, a
+    # batch of three with an 8-column last tile, fewer tiles than workgroups, and an
+    # image narrower and shorter than one tile
     ("c64_pers_ragged", (S_(2, 64, 130, 200, 3), 120)), ("c64_pers_batch3_w136", (S_(3, 64, 64, 136, 3), 121)),
+    ("c64_pers_few_tiles", (S_(1, 64, 10, 72, 3), 122)), ("c64_pers_w8_h3", (S_(2, 64, 3, 8, 3), 123)),
 ]
 
 BWD_CASES = [
