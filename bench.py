@@ -82,15 +82,17 @@ KERNEL_BOUND = {"filter": "hbm", "fused_fwd": "mfma", "bwd_dx": "mfma", "bwd_dy"
 
 # Kernel symbol and the source files that define it (for the traffic record's digest).
 # dX at C = 64 on grids of more than two row segments per CU runs the row-staged
-# kernels of bwd_dx_rows.hip (one per dtype).
-KERNEL_SYMBOL = {"filter": "filter_fwd_kernel", "fused_fwd": "fused_fwd_kernel",
+# kernels of bwd_dx_rows.hip (one per dtype); the bfloat16 forward at K = 3, C = 64
+# runs the persistent kernel of fused_fwd_pers.hip.
+KERNEL_SYMBOL = {"filter": "filter_fwd_kernel",
+                 "fused_fwd": {"f32": "fused_fwd_kernel", "bf16": "fused_fwd_pers_kernel"},
                  "bwd_dx": {"f32": "bwd_dx_f32_kernel", "bf16": "bwd_dx_bf16_kernel"},
                  "bwd_dy": {"f32": "bwd_dy_f32_kernel", "bf16": "bwd_dy_bf16_kernel"},
                  "bwd_dw": "bwd_dw_rows_kernel", "reduce": "reduce_partials_kernel",
                  "filter_bwd": "filter_bwd_kernel"}
 KERNEL_SOURCES = {
     "filter": ["filter_fwd.hip", "common.hpp"],
-    "fused_fwd": ["fused_fwd.hip", "gen_mma.hpp", "common.hpp"],
+    "fused_fwd": ["fused_fwd.hip", "fused_fwd_pers.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dx": ["bwd_dx.hip", "bwd_dx_rows.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dy": ["fused_bwd.hip", "bwd_dy_rows.hip", "gen_mma.hpp", "common.hpp"],
     "bwd_dw": ["fused_bwd.hip", "bwd_dw_rows.hip", "gen_mma.hpp", "common.hpp"],

@@ -18,6 +18,11 @@
 // four-wave groups, one per dilation branch, sharing the staged x tile.
 // y is read once per wave into registers (the MFMA B operand is the same for
 // all 3*K*K generator blocks) when C <= 64; larger C streams it per block.
+// bfloat16 at K = 3 and C = 64 (W % 8 == 0, 16-byte aligned tensors) goes to the
+// persistent kernel of fused_fwd_pers.hip instead: same arithmetic, tiles streamed
+// into LDS behind the compute.
+// The staged x planes of channels 4g..4g+3 (lane group g) are shifted by g floats
+// so that the four groups' reads fall on different LDS banks.
 #include <algorithm>
 #include <type_traits>
 

@@ -112,7 +112,12 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
     constexpr int nCB = C / 16;
     const int L = xcd_contiguous(blockIdx.x, gridDim.x);
     const int c0 = (L % nCB) * 16;
-    const int m = L / nCB, per = gridDim.x / nCB;  // this workgroup's tiles: m, m + per, ...
+    // This workgroup's tiles: the run [m * T, m * T + T) of the (image, row band, column
+    // tile) order, so that at each step the workgroups of one XCD (consecutive m) work
+    // on neighbouring bands and take each other's halo rows from their shared L2.
+    const int m = L / nCB, per = gridDim.x / nCB;
+    const int T = (S + per - 1) / per;
+    const int st0 = m * T, st1 = min(S, st0 + T);
 
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, xbytes), ry = rsrc(y, xbytes);
     const __amdgpu_buffer_rsrc_t rw = rsrc(wg, 3u * C * KK * C * 2u), ro = rsrc(out, obytes);
@@ -150,17 +155,13 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
         xrel[k] = (ch * HW + (row - PT::HALO) * W + chunk * 8 - 8) * 2;
         xrc[k] = ((row - PT::HALO) & 0xffff) | ((chunk * 8 - 8) * 65536);
     }
-    // The tiles m, m + per, ... in (image, row band, column tile) order, walked with
-    // carries instead of divisions.
+    // tile coordinates, advanced by carries instead of divisions
     struct Tile { int n, band, colt; };
-    const int dcol = per % ncolt, drest = per / ncolt;
-    const int dband = drest % nbands, dn = drest / nbands;
     auto advance = [&](Tile t) {
-        t.colt += dcol;
-        if (t.colt >= ncolt) { t.colt -= ncolt; ++t.band; }
-        t.band += dband;
-        if (t.band >= nbands) { t.band -= nbands; ++t.n; }
-        t.n += dn;
+        if (++t.colt == ncolt) {
+            t.colt = 0;
+            if (++t.band == nbands) { t.band = 0; ++t.n; }
+        }
         return t;
     };
     auto issue_x = [&](Tile tl, int buf) {
@@ -201,12 +202,14 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
     const char *wb = sm + PT::OFF_W + b * KK * 2048;
     const float *bl = (const float *)(sm + PT::OFF_B) + b * KK * 16 + 4 * g;
 
-    Tile cur = {m / (ncolt * nbands), (m / ncolt) % nbands, m % ncolt};
-    issue_x(cur, 0);
-    issue_y(cur);
+    Tile cur = {st0 / (ncolt * nbands), (st0 / ncolt) % nbands, st0 % ncolt};
+    if (st0 < st1) {  // (a workgroup past the last run has no tiles)
+        issue_x(cur, 0);
+        issue_y(cur);
+    }
     int it = 0;
 #pragma unroll 1
-    for (int st = m; st < S; st += per, ++it) {
+    for (int st = st0; st < st1; ++st, ++it) {
         // Every wave's loads of this tile have landed (the stores of the previous tile,
         // issued after them, may still be in flight), and every wave is done with the
         // previous tile's x buffer.
@@ -217,9 +220,9 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
         else
             barrier_after<4>();
         const int buf = it & 1;
-        const int nxt = st + per;
+        const bool more = st + 1 < st1;
         const Tile tnx = advance(cur);
-        if (nxt < S) issue_x(tnx, buf ^ 1);
+        if (more) issue_x(tnx, buf ^ 1);
 
         // the generator's B operand: y of this row, channels 32q + 8g + e, pixel 4j + pb
         Gen<bf16_t>::BFrag bres[2];
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(768, 1) void fused_fwd_pers_kernel(const bf16_t *__
             }
         }
         barrier_after<63>();  // every wave holds its y operand before the next tile's y lands
-        if (nxt < S) issue_y(tnx);
+        if (more) issue_y(tnx);
 
         const char *xb = sm + PT::OFF_X + buf * PT::XBUF + xl;
         // x of tap t at pixel 4j + pb, channel 4g + v: dwords at an aligned start, the
