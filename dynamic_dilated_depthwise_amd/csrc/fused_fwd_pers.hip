@@ -390,8 +390,11 @@ hipError_t launch_fused_fwd_pers(const void *x, const void *y, const void *wg, c
                                  int H, int W, hipStream_t stream) {
     constexpr int C = PT::C;
     const int64_t S = (int64_t)N * ((H + 3) / 4) * ((W + 63) / 64);
+    // at most one workgroup per CU (256 CUs, C / 16 channel blocks each taking a
+    // quarter), and no more per block than the runs of T tiles need
     constexpr int kCUs = 256;
-    const int per = (int)std::min<int64_t>(S, kCUs / (C / 16));
+    const int64_t T = (S + kCUs / (C / 16) - 1) / (kCUs / (C / 16));
+    const int per = (int)((S + T - 1) / T);
     const unsigned xbytes = (unsigned)((int64_t)N * C * H * W * 2);
     hipError_t e = hipFuncSetAttribute((const void *)fused_fwd_pers_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, PT::BYTES);
