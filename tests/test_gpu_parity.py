@@ -49,6 +49,8 @@ FWD_CASES = [
     # image narrower and shorter than one tile
     ("c64_pers_ragged", (S_(2, 64, 130, 200, 3), 120)), ("c64_pers_batch3_w136", (S_(3, 64, 64, 136, 3), 121)),
     ("c64_pers_few_tiles", (S_(1, 64, 10, 72, 3), 122)), ("c64_pers_w8_h3", (S_(2, 64, 3, 8, 3), 123)),
+    # the same channel count with W % 8 != 0: bfloat16 stays on the per-tile kernel
+    ("c64_w68_per_tile", (S_(1, 64, 12, 68, 3), 124)),
 ]
 
 BWD_CASES = [
