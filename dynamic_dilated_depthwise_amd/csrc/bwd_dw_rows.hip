@@ -70,7 +70,6 @@ template <typename T, int K> struct DwPlan {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x8_a2 __attribute__((ext_vector_type(8), aligned(2)));
 
 // WHOLE: the batch's y, x and gradient tensors each fit one buffer resource (the
 // host checks the byte sizes): the resources are built once and an image is a scalar
@@ -316,8 +315,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_rows_kernel(const T *__restrict
             for (int nb = 0; nb < 4; ++nb) yv[nb] = __builtin_bit_cast(bf16x8, *(const u16x8 *)(ys + 16 * nb * P::YR));
 #pragma unroll
             for (int kj = 0; kj < NGRP; ++kj) {
-                const u16x8 xr = *(const u16x8_a2 *)(xs + (kj - r) * D);
-                const u32x4 xw = __builtin_bit_cast(u32x4, xr);
+                // x at column offset (kj - r) * D: the dilations are odd, so the offset's
+                // parity is that of kj - r (a constant).  At K = 3 an odd offset is read
+                // as five aligned dwords from one element earlier and shifted down by 16
+                // bits (2 % faster than one 2-byte-aligned 16-byte LDS read); at K = 5
+                // the extra registers cost more than the aligned reads save.
+                u32x4 xw;
+                if (K <= 3 && ((kj - r) & 1)) {
+                    const uint32_t *q = (const uint32_t *)(xs + (kj - r) * D - 1);
+                    uint32_t d5[5];
+#pragma unroll
+                    for (int m = 0; m < 5; ++m) d5[m] = q[m];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) xw[m] = __builtin_amdgcn_perm(d5[m + 1], d5[m], 0x05040302u);
+                } else {
+                    typedef uint16_t u16x8_a2 __attribute__((ext_vector_type(8), aligned(2)));
+                    xw = __builtin_bit_cast(u32x4, *(const u16x8_a2 *)(xs + (kj - r) * D));
+                }
+                const u16x8 xr = __builtin_bit_cast(u16x8, xw);
                 u16x8 u;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
