@@ -237,9 +237,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
     // tap.  A pair's two rounded taps meet G_b at their two source pixels in one
     // two-term bf16 dot product with float32 accumulation (v_dot2_f32_bf16), which
     // sums the pair's two exact products into the running sum.  An item (a pair or
-    // single, one pixel block) is applied after the next item's MFMAs, across stage
-    // boundaries too (it only touches registers), so its MFMA results are not waited
-    // for right away.  pacc / pg: the pending item, pend: whether there is one.
+    // single, one pixel block) is applied after the next item's MFMAs of the same
+    // stage, so its MFMA results are not waited for right away; a stage's last item
+    // is applied at the stage's end.  pacc / pg: the pending item, pend: whether
+    // there is one.
     constexpr int NPAIR = K / 2;
     constexpr int NGRP = (K + 1) / 2;
     f32x4 pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -339,12 +340,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
                     acc[u] = mfma_16x16x32_bf16(o.a0[u], cur.b0, bias4[u]);
                     acc[u] = mfma_16x16x32_bf16(o.a1[u], cur.b1, acc[u]);
                 }
-                // the pending item: the previous one of this stage, else the last
-                // item (pixel block 3 of the last group) of an earlier stage
+                // the pending item: the previous one of this stage
                 if (pend) {
                     if (pb > 0) retire(pair, pb - 1);
-                    else if (gi > 0) retire(gi - 1 < NPAIR, 3);
-                    else retire(NGRP - 1 < NPAIR, 3);
+                    else retire(gi - 1 < NPAIR, 3);
                 }
                 pacc[0] = acc[0];
 #pragma unroll
@@ -357,13 +356,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
                 pend = true;
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // The stage's last item is applied before the stage ends, so that no
+            // pending value is live across the branch that skips a stage (the two
+            // paths would otherwise merge it through register copies).
+            retire(NGRP - 1 < NPAIR, 3);
+            pend = false;
         } else {
 #pragma unroll
             for (int gi = 0; gi < NGRP; ++gi) fetch_upto(st, gi);
-            if (pend) {  // the pending item is the last of an earlier stage
-                retire(NGRP - 1 < NPAIR, 3);
-                pend = false;
-            }
         }
         if (st + 1 < NST) {
             store_stage(st + 1, (st + 1) & 1);
@@ -372,7 +372,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
         }
     }
 
-    if (pend) retire(NGRP - 1 < NPAIR, 3);
 
     // dX = G_x + the gathered sum, rounded once
     const bf16_t *gxr = gn + c * HW + h * W + w0 + 4 * g;
