@@ -70,14 +70,12 @@ template <typename T, int K> struct DwPlan {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_a2 __attribute__((ext_vector_type(8), aligned(2)));
 
 // WHOLE: the batch's y, x and gradient tensors each fit one buffer resource (the
 // host checks the byte sizes): the resources are built once and an image is a scalar
 // offset, so a segment's loads cost no descriptor or 64-bit pointer arithmetic.
-// FULL (with WHOLE): W is a multiple of the segment, so every segment of a range is
-// whole and inside one row (the ranges start and end at multiples of the segment),
-// and a segment's length is SEG, or 0 past the range.
-template <typename T, int K, bool WHOLE, bool FULL = false>
+template <typename T, int K, bool WHOLE>
 __global__ __launch_bounds__(256, 2) void bwd_dw_rows_kernel(const T *__restrict__ x, const T *__restrict__ y,
                                                              const T *__restrict__ gout, float *__restrict__ dw_part,
                                                              float *__restrict__ db_part, int N, int H, int W, int S) {
@@ -169,15 +167,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_rows_kernel(const T *__restrict
         __builtin_amdgcn_make_buffer_rsrc((void *)gout, 0, WHOLE ? N * 4 * C * HW * P::ES : 0, W3);
     const __amdgpu_buffer_rsrc_t wx = __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, WHOLE ? N * C * HW * P::ES : 0, W3);
     auto load_seg = [&](Regs &o) {  // the segment at the cursor -> o; advances the cursor
-        int len;
-        if constexpr (FULL) {
-            len = tl < tend ? SEG : 0;
-        } else {
-            const TokT left = tend - tl;  // may be <= 0 past the range: every slot reads zero
-            const int lc = left < 0 ? 0 : (left > SEG ? SEG : (int)left);
-            const int wl = W - lw;
-            len = lc < wl ? lc : wl;
-        }
+        const TokT left = tend - tl;  // may be <= 0 past the range: every slot reads zero
+        const int lc = left < 0 ? 0 : (left > SEG ? SEG : (int)left);
+        const int wl = W - lw;
+        const int len = lc < wl ? lc : wl;
         const __amdgpu_buffer_rsrc_t ry =
             WHOLE ? wy : __builtin_amdgcn_make_buffer_rsrc((void *)yb, 0, C * HW * P::ES, W3);
         const __amdgpu_buffer_rsrc_t rg =
@@ -186,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_rows_kernel(const T *__restrict
             WHOLE ? wx : __builtin_amdgcn_make_buffer_rsrc((void *)xb, 0, 16 * HW * P::ES, W3);
         const int by = iy, bgo = ig, bx = ix;  // the image's scalar offsets (zero unless WHOLE)
         const int soff = (lh * W + lw) * P::ES;
-        const bool yok = FULL ? len > 0 : ycol < len;  // (FULL: wave-uniform)
+        const bool yok = ycol < len;
 #pragma unroll
         for (int k = 0; k < P::YIT; ++k)
             o.y[k] = __builtin_bit_cast(u32x4,
@@ -323,10 +316,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dw_rows_kernel(const T *__restrict
             for (int nb = 0; nb < 4; ++nb) yv[nb] = __builtin_bit_cast(bf16x8, *(const u16x8 *)(ys + 16 * nb * P::YR));
 #pragma unroll
             for (int kj = 0; kj < NGRP; ++kj) {
-                // x at column offset (kj - r) * D: one 16-byte LDS read, 2-byte aligned
-                // for odd offsets.  (Five aligned dwords realigned by v_perm_b32 ran 3-4 %
-                // faster at K = 3 but issue 0.8 more instructions per MFMA; kept out.)
-                typedef uint16_t u16x8_a2 __attribute__((ext_vector_type(8), aligned(2)));
                 const u16x8 xr = *(const u16x8_a2 *)(xs + (kj - r) * D);
                 const u32x4 xw = __builtin_bit_cast(u32x4, xr);
                 u16x8 u;
@@ -435,8 +424,7 @@ static hipError_t launch_dw_rows_t(const void *x, const void *y, const void *gou
         Elem<T>::is_bf16 && (int64_t)N * 4 * kChW * H * W * (int64_t)sizeof(T) < (int64_t)0x7ffffff0;
     auto kern = bwd_dw_rows_kernel<T, K, false>;
     if constexpr (Elem<T>::is_bf16) {
-        // rows of whole segments: no per-segment length or bounds arithmetic
-        if (whole) kern = W % DwPlan<T, K>::SEG == 0 ? bwd_dw_rows_kernel<T, K, true, true> : bwd_dw_rows_kernel<T, K, true>;
+        if (whole) kern = bwd_dw_rows_kernel<T, K, true>;
     }
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
