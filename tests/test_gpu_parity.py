@@ -196,6 +196,29 @@ def test_filter_bwd_one_output(name, dt, want):
     _check_filter_bwd(gx, gk, ref, dtype, f"filter_bwd[{want}] {name} {dt}")
 
 
+@pytest.mark.parametrize("shape", [S_(1, 64, 20, 72, 3), S_(2, 64, 9, 136, 3)], ids=["20x72", "batch2_9x136"])
+def test_persistent_forward_bit_identical_to_per_tile(shape):
+    """The persistent bf16 forward (K = 3, C = 64, 16-byte aligned tensors) and the
+    per-tile kernel (taken when a pointer is only element-aligned) compute the same
+    MFMA fragments, the same rounded taps and the same pair sums in the same order:
+    their outputs agree bit for bit."""
+    h = inputs(shape, 304, torch.bfloat16)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, device="cuda", dtype=t.dtype)
+        v = buf[1:].view(t.shape)
+        v.copy_(t.to("cuda"))
+        return v
+
+    announce("persistent vs per-tile", shape)
+    aligned = gpu_fused(dev(h), shape.K)
+    d = {k: shifted(v) for k, v in h.items()}
+    assert d["x"].data_ptr() % 16 != 0
+    per_tile = gpu_fused(d, shape.K)
+    torch.cuda.synchronize()
+    assert torch.equal(aligned.view(torch.int16), per_tile.view(torch.int16))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_misaligned_pointers(dt):
     """Element-aligned (not 16-byte aligned) tensors take the scalar/unaligned paths."""
