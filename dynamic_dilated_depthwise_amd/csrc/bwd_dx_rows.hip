@@ -396,11 +396,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_bf16_kernel(const bf16_t *__res
 // (four 16-byte LDS reads) and its B values 16 contiguous weights of one row (four
 // 16-byte loads).  A tap is 64 MFMAs per wave.  Per (branch, kernel row) stage, y
 // is staged as [pixel][64 channels + 4 pad] (272-byte pixel rows: the 16 pixels of
-// a fragment start in distinct 4-dword bank groups) and G_b as channel rows of 84
-// floats (the 16 channels of a read start in distinct 4-dword bank groups), each
-// once per stage and read at the K column shifts of its taps; one LDS image,
-// written between two barriers, its global loads issued a whole stage ahead.  The
-// weight rows come from global memory one tap ahead.
+// a fragment start in distinct 4-dword bank groups) in one of two LDS images: the
+// next stage's row is loaded at the start of a stage and written into the other
+// image after the stage's first tap, so one barrier per stage suffices.  G_b is
+// staged as channel rows of GROW floats (the 16 channels of a read start in
+// distinct 4-dword bank groups); each wave reads only its own 16 channel rows, so
+// it stages them itself, at the end of a stage, with no barrier.  G_b runs start at
+// a column shift that is a compile-time constant per tap; shifts that are not a
+// multiple of four are read as two aligned 16-byte words.  The weight rows come
+// from global memory one tap ahead.
 template <int K> struct DxPlanF {
     static constexpr int r = (K - 1) / 2;
     static constexpr int KK = K * K;
@@ -410,9 +414,10 @@ template <int K> struct DxPlanF {
     static constexpr int LP = (HALO + 3) & ~3;
     static constexpr int SW = kSegX + 2 * LP;
     static constexpr int PROW = kChX + 4;         // floats per staged y pixel
-    static constexpr int YBUF = SW * PROW;        // floats of the staged y row
+    static constexpr int YBUF = SW * PROW;        // floats of one staged y row
     static constexpr int GROW = ((SW + 12) / 16) * 16 + 4;  // floats per staged G channel row (== 4 mod 16)
-    static constexpr int GBUF = kChX * GROW;      // floats of the staged G row
+    static constexpr int GBUF = kChX * GROW;      // floats of the staged G rows (16 per wave)
+    static constexpr int BYTES = 4 * (2 * YBUF + GBUF);
     // Stage order: the 3(K-1) (branch, kernel row) pairs with a row shift first
     // (branch-major), then the three unshifted kernel rows (ki = r) of branches
     // 0, 1, 2, which read the same y row and stage it once.
@@ -421,7 +426,13 @@ template <int K> struct DxPlanF {
     static constexpr int stage_b(int s) { return s < NSHIFT ? s / KM : s - NSHIFT; }
     static constexpr int stage_ki(int s) { return s < NSHIFT ? (s % KM < r ? s % KM : s % KM + 1) : r; }
     static constexpr bool new_y(int s) { return s <= NSHIFT; }  // stage s stages its own y row
+    static constexpr int y_image(int s) { return (s < NSHIFT ? s : NSHIFT) & 1; }
 };
+
+// Barrier for the staged y rows: this wave's LDS operations complete, then every
+// wave of the workgroup arrives.  Outstanding global loads (the next stage's rows,
+// the next tap's weights) stay in flight; their registers are waited for where used.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int K>
 __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restrict__ y,
@@ -435,8 +446,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
     constexpr int NT = P::NT;
     constexpr int NST = P::NST;
     constexpr int C = kChX;
-    __shared__ __align__(16) float ys[P::YBUF];
-    __shared__ __align__(16) float gs[P::GBUF];
+    extern __shared__ __align__(16) float dsm[];
+    float *const ys = dsm;                  // two y images of YBUF floats
+    float *const gs = dsm + 2 * P::YBUF;    // G_b channel rows
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -456,12 +468,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
 
     // ---- staging.  y: thread tid covers blocks of 4 channels x 4 pixels, transposed
     // in registers into four pixel entries of 4 channels; G_b: runs of 4 pixels of
-    // one channel row, copied as they are.  Runs outside the image (W % 4 == 0:
-    // wholly in or out) load the row's first run and are zeroed.
+    // one of the wave's channel rows, copied as they are.  Runs outside the image
+    // (W % 4 == 0: wholly in or out) load the row's first run and are zeroed.
     constexpr int NB4 = P::SW / 4;
     constexpr int YIT = (NB4 + 15) / 16;   // y blocks per thread (16 runs of 4 pixels per iteration)
-    constexpr int NRUN = kChX * NB4;
-    constexpr int GIT = (NRUN + 255) / 256;
+    constexpr int NRUN = 16 * NB4;         // G_b runs of one wave
+    constexpr int GIT = (NRUN + 63) / 64;
     f32x4 yreg[YIT][4];
     f32x4 greg[GIT];
     unsigned yoff[YIT], goff[GIT];
@@ -483,52 +495,55 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
     }
 #pragma unroll
     for (int k = 0; k < GIT; ++k) {
-        const int q = tid + 256 * k;
+        const int q = lane + 64 * k;
         const int ch = q / NB4;
         const int px4 = q - ch * NB4;
         const int col = w0 - P::LP + 4 * px4;
         gex[k] = q < NRUN;
         gok[k] = gex[k] && col >= 0 && col < W;
-        goff[k] = (unsigned)((gex[k] ? ch : 0) * HW + (gok[k] ? col : 0));
-        gdst[k] = ch * P::GROW + 4 * px4;
+        goff[k] = (unsigned)((16 * wave + (gex[k] ? ch : 0)) * HW + (gok[k] ? col : 0));
+        gdst[k] = (16 * wave + ch) * P::GROW + 4 * px4;
     }
     auto stage_row = [&](int st) {  // the stage's source row (may lie outside the image)
         return h - (P::stage_ki(st) - r) * (1 + 2 * P::stage_b(st));
     };
+    // Loads of stage st, unconditional: a row outside the image loads the nearest
+    // image row instead, whose staged copy no tap reads (its taps are skipped), so
+    // no branch holds the loaded registers and nothing waits for them before they
+    // are stored.  y goes first, so that waiting for it leaves the G_b loads in flight.
     auto load_stage = [&](int st) {
-        const int hs = stage_row(st);
-        if (hs < 0 || hs >= H) return;  // wave-uniform: the stage is skipped
-        const float *ybase = yn + hs * W;
-        const float *gbase = gn + (1 + P::stage_b(st)) * C * HW + hs * W;
+        const int hr = stage_row(st);
+        const int hs = hr < 0 ? 0 : (hr >= H ? H - 1 : hr);
         if (P::new_y(st)) {
+            const float *ybase = yn + hs * W;
 #pragma unroll
             for (int k = 0; k < YIT; ++k)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f32x4 v = *(const f32x4 *)(ybase + (yoff[k] + (unsigned)(e * HW)));
-                    yreg[k][e] = yok[k] ? v : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                for (int e = 0; e < 4; ++e) yreg[k][e] = *(const f32x4 *)(ybase + (yoff[k] + (unsigned)(e * HW)));
         }
+        const float *gbase = gn + (1 + P::stage_b(st)) * C * HW + hs * W;
 #pragma unroll
-        for (int k = 0; k < GIT; ++k) {
-            const f32x4 v = *(const f32x4 *)(gbase + goff[k]);
-            greg[k] = gok[k] ? v : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int k = 0; k < GIT; ++k) greg[k] = *(const f32x4 *)(gbase + goff[k]);
     };
-    auto store_stage = [&](int st) {
-        const int hs = stage_row(st);
-        if (hs < 0 || hs >= H) return;
+    // Runs outside the image (columns) are written as zeros.
+    auto store_y = [&](int st) {
+        if (!P::new_y(st)) return;
+        float *img = ys + P::y_image(st) * P::YBUF;
 #pragma unroll
         for (int k = 0; k < YIT; ++k) {
-            if (!P::new_y(st) || !yex[k]) continue;
-            float *d = ys + ydst[k];
+            if (!yex[k]) continue;
+            float *d = img + ydst[k];
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
-                *(f32x4 *)(d + p * P::PROW) = f32x4{yreg[k][0][p], yreg[k][1][p], yreg[k][2][p], yreg[k][3][p]};
+            for (int p = 0; p < 4; ++p) {
+                const f32x4 v = {yreg[k][0][p], yreg[k][1][p], yreg[k][2][p], yreg[k][3][p]};
+                *(f32x4 *)(d + p * P::PROW) = yok[k] ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
+    };
+    auto store_g = [&]() {
 #pragma unroll
         for (int k = 0; k < GIT; ++k)
-            if (gex[k]) *(f32x4 *)(gs + gdst[k]) = greg[k];
+            if (gex[k]) *(f32x4 *)(gs + gdst[k]) = gok[k] ? greg[k] : f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
     // ---- weight rows from global memory, one tap ahead: tap (b, t) for channel c,
@@ -554,9 +569,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
 #pragma unroll
         for (int v = 0; v < 4; ++v) dacc[pb][v] = 0.f;
 
-    WOps ring[2];  // operands of the ti-th tap of the stage order in ring[ti & 1]
+    // Tap ti of the stage order (stage ti / K, kernel column ti % K) as b*KK + t.
+    auto tap_bt = [&](int ti) {
+        const int sn = ti / K;
+        return P::stage_b(sn) * KK + P::stage_ki(sn) * K + ti % K;
+    };
+    // Operands of tap ti in ring[ti % 3], fetched two taps ahead: a stage's loads
+    // are issued at its start, after the weights of its first two taps, so only
+    // the third tap's weights wait for them (load counters retire in order).
+    WOps ring[3];
     load_stage(0);
-    fetch(P::stage_b(0) * KK + P::stage_ki(0) * K, ring[0]);
+    store_y(0);
+    store_g();
+    fetch(tap_bt(0), ring[0]);
+    if (NT > 1) fetch(tap_bt(1), ring[1]);
     // A fragment: pixel 16pb + i + (LP - dc), channels 16g .. 16g + 15
     const int a_lane = i * P::PROW + 16 * g;
     // G_b run: channel c, pixels 16pb + 4g + (LP - dc) .. +3
@@ -568,23 +594,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
         const int D = 1 + 2 * b;
         const int hs = h - (ki - r) * D;
         const bool rok = hs >= 0 && hs < H;  // wave-uniform: taps reading outside the image add nothing
-        if (st > 0) __syncthreads();  // every wave is done reading the previous stage
-        store_stage(st);
-        __syncthreads();
+        lds_barrier();  // y of this stage written; every wave done reading the image it replaces
         if (st + 1 < NST) load_stage(st + 1);
+        const float *yimg = ys + P::y_image(st) * P::YBUF;
 #pragma clang loop unroll(full)
         for (int kj = 0; kj < K; ++kj) {
             const int ti = st * K + kj;  // position in the tap order
-            const WOps &cur = ring[ti & 1];
-            if (ti + 1 < NT) {
-                const int sn = (kj + 1 < K) ? st : st + 1;
-                const int kn = (kj + 1 < K) ? kj + 1 : 0;
-                fetch(P::stage_b(sn) * KK + P::stage_ki(sn) * K + kn, ring[(ti + 1) & 1]);
-            }
+            const WOps &cur = ring[ti % 3];
+            if (ti + 2 < NT) fetch(tap_bt(ti + 2), ring[(ti + 2) % 3]);
             if (rok) {
                 const int dc = (kj - r) * D;
-                const float *ab = ys + a_lane + (P::LP - dc) * P::PROW;
-                const float *gb = gs + g_lane + (P::LP - dc);
+                const float *ab = yimg + a_lane + (P::LP - dc) * P::PROW;
+                const int go = P::LP - dc;     // a constant once the loops are unrolled
+                const int gm = go & 3;         // misalignment of the G_b run in floats
+                const float *gb = gs + g_lane + (go - gm);
                 // the A reads of block pb + 1 are issued before block pb's MFMAs
                 f32x4 a[2][4];
 #pragma unroll
@@ -596,7 +619,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
                         for (int q = 0; q < 4; ++q)
                             a[(pb + 1) & 1][q] = *(const f32x4 *)(ab + (pb + 1) * 16 * P::PROW + 4 * q);
                     }
-                    const f32x4 gv = *(const f32x4_a4 *)(gb + 16 * pb);
+                    const f32x4 g0 = *(const f32x4 *)(gb + 16 * pb);
+                    f32x4 gv = g0;
+                    if (gm != 0) {
+                        const f32x4 g1 = *(const f32x4 *)(gb + 16 * pb + 4);
+                        if (gm == 1) gv = f32x4{g0[1], g0[2], g0[3], g1[0]};
+                        else if (gm == 2) gv = f32x4{g0[2], g0[3], g1[0], g1[1]};
+                        else gv = f32x4{g0[3], g1[0], g1[1], g1[2]};
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                     f32x4 acc = {cur.bias, cur.bias, cur.bias, cur.bias};
 #pragma unroll
@@ -607,6 +637,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
                     for (int v = 0; v < 4; ++v) dacc[pb][v] += acc[v] * gv[v];
                 }
             }
+            // the next stage's y row goes into the other image once its loads have had two
+            // taps' time (K = 1: one)
+            if (kj == (K > 1 ? 1 : 0) && st + 1 < NST) store_y(st + 1);
+        }
+        if (st + 1 < NST) {
+            // this wave's G_b rows: its reads of this stage are issued (LDS executes a
+            // wave's operations in order); keep the compiler from moving them across
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            store_g();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
         }
     }
 
@@ -633,6 +675,21 @@ bool bwd_dx_rows_applies(int C, int H, int W, bool al, bool bf16) {
     return C == kChX && al && (W % 4) == 0 && (int64_t)4 * kChX * H * W * (bf16 ? 2 : 1) < (int64_t(1) << 31);
 }
 
+namespace {
+template <int K>
+hipError_t launch_dx_f32(dim3 grid, hipStream_t stream, const float *y, const float *wg, const float *bg,
+                         const float *gout, float *gx, int H, int W) {
+    constexpr int bytes = DxPlanF<K>::BYTES;
+    if (bytes > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void *)bwd_dx_f32_kernel<K>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(bwd_dx_f32_kernel<K>, grid, dim3(256), bytes, stream, y, wg, bg, gout, gx, H, W);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_bwd_dx_rows(const void *y, const void *wg, const void *bg, const void *gout, void *gx, int N,
                               int H, int W, int K, bool bf16, hipStream_t stream) {
     const int64_t nblk = (int64_t)N * H * ((W + kSegX - 1) / kSegX);
@@ -642,11 +699,10 @@ hipError_t launch_bwd_dx_rows(const void *y, const void *wg, const void *bg, con
         const float *Y = (const float *)y, *Wg = (const float *)wg, *Bg = (const float *)bg, *G = (const float *)gout;
         float *GX = (float *)gx;
         switch (K) {
-            case 1: hipLaunchKernelGGL(bwd_dx_f32_kernel<1>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
-            case 3: hipLaunchKernelGGL(bwd_dx_f32_kernel<3>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
-            default: hipLaunchKernelGGL(bwd_dx_f32_kernel<5>, grid, block, 0, stream, Y, Wg, Bg, G, GX, H, W); break;
+            case 1: return launch_dx_f32<1>(grid, stream, Y, Wg, Bg, G, GX, H, W);
+            case 3: return launch_dx_f32<3>(grid, stream, Y, Wg, Bg, G, GX, H, W);
+            default: return launch_dx_f32<5>(grid, stream, Y, Wg, Bg, G, GX, H, W);
         }
-        return hipGetLastError();
     }
     const bf16_t *Y = (const bf16_t *)y, *Wg = (const bf16_t *)wg, *Bg = (const bf16_t *)bg,
                  *G = (const bf16_t *)gout;

@@ -209,11 +209,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dy_f32_kernel(const float *__restr
             if (bt + 1 < NT) fetch(bt + 1, ring[(bt + 1) & 1]);
             if (rok) {
                 const int dc = (kj - r) * D;
+                // the x run starts dc columns off an aligned word (a constant once the
+                // loops are unrolled); an unaligned start reads two aligned 16-byte words
+                const int xo = P::LP + dc;
+                const int xm = xo & 3;
                 __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const f32x4 gv = *(const f32x4 *)(gsb + g_lane + 4 * s * P::GROW);
-                    const f32x4 xv = *(const f32x4_a4 *)(xs + x_lane + 4 * s * P::XROW + P::LP + dc);
+                    const float *xa = xs + x_lane + 4 * s * P::XROW + (xo - xm);
+                    const f32x4 x0 = *(const f32x4 *)xa;
+                    f32x4 xv = x0;
+                    if (xm != 0) {
+                        const f32x4 x1 = *(const f32x4 *)(xa + 4);
+                        if (xm == 1) xv = f32x4{x0[1], x0[2], x0[3], x1[0]};
+                        else if (xm == 2) xv = f32x4{x0[2], x0[3], x1[0], x1[1]};
+                        else xv = f32x4{x0[3], x1[0], x1[1], x1[2]};
+                    }
                     f32x4 dk;
 #pragma unroll
                     for (int pb = 0; pb < 4; ++pb) dk[pb] = gv[pb] * xv[pb];
