@@ -575,8 +575,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_f32_kernel(const float *__restr
         return P::stage_b(sn) * KK + P::stage_ki(sn) * K + ti % K;
     };
     // Operands of tap ti in ring[ti % 3], fetched two taps ahead: a stage's loads
-    // are issued at its start, after the weights of its first two taps, so only
-    // the third tap's weights wait for them (load counters retire in order).
+    // are issued at its start, after the weights of its first two taps, so those
+    // two taps never wait for them (load counters retire in order).
     WOps ring[3];
     load_stage(0);
     store_y(0);
