@@ -78,6 +78,9 @@ BWD_CASES = [
     # two at K = 1 with a ragged 136-column row
     ("c64_k5_w200_tall", (S_(1, 64, 264, 200, 5), 223)), ("c64_w264_two_seg", (S_(1, 64, 130, 264, 3), 224)),
     ("c64_k1_batch2_w136", (S_(2, 64, 128, 136, 1), 225)),
+    # images shorter than the K = 5 reach (rows up to 10 away): on the row-staged
+    # kernels most stages lie above or below the image at once
+    ("c64_k5_short_images", (S_(16, 64, 8, 128, 5), 229)),
     # C = 64 grids too small for the 128-pixel halves (the bf16 dY quarters: 64-pixel
     # segments x 16 output channels): one segment per row, a ragged second segment at
     # K = 5, and K = 1 with a ragged 120-column row
